@@ -1,0 +1,303 @@
+"""Benchmark of the per-row MoE route on one MI355X.
+
+One step = one route_fused call (latent down projection 7168 -> 3584 in BF16,
+FP32 router logits over 896 experts, standalone top-16) over one batch of
+synthetic rows, inputs and weights resident in HBM. The headline workload is
+the 8-row decode round; the weights rotate over 8 distinct copies (8 x 77 MB,
+more than the 256 MB Infinity Cache) so every step streams its weights from
+HBM. Steps are replayed from a HIP graph holding 8 route_fused calls (one per
+weight copy, each on its own input bank); K steps = K/8 replays, timed with
+events on the launch stream between two device synchronisations.
+
+Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows) and
+the 3072-row prefill chunk, the decode kernel's HBM roofline fraction, the
+prefill MFMA fraction, and the CPU oracle timed on this host (a reported
+baseline only).
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "us per MoE-layer route (1-20 rows) + prefill rows/s; % HBM / MFMA peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+K, N, E = 7168, 3584, 896
+FIXED_BYTES = K * N * 2 + K * E * 4                       # 77,070,336
+ROW_BYTES = K * 2 + N * 2 + E * 4 + 16 * 4 + 16 * 4       # 25,216
+PREFILL_FLOPS_LATENT = 2.0 * 3072 * K * N                 # 157.84 GFLOP
+PREFILL_FLOPS_ROUTER_MFMA = 3 * 2.0 * 3072 * K * E        # bf16 x3 split, 118.4 GFLOP
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_route_r8_counters.md")
+DECODE_SOURCES = ["latent_projection_top_amd/csrc/decode_route.hip",
+                  "latent_projection_top_amd/csrc/route_device.h"]
+
+
+def decode_bytes(rows: int) -> int:
+    return FIXED_BYTES + ROW_BYTES * rows
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    fields = {}
+    for line in open(PROFILE_COUNTERS):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_digest") != source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class DecodeSetup:
+    def __init__(self, rows: int, copies, banks_dev, route, torch):
+        self.rows = rows
+        self.route = route
+        self.torch = torch
+        self.plan = route.Plan(route.MODE_DECODE, rows)
+        n = len(copies)
+        self.ws = [self.plan.new_workspace() for _ in range(n)]
+        self.xs = [banks_dev[i][:rows].contiguous() for i in range(n)]
+        dev = "cuda"
+        self.lat = torch.empty((n, rows, N), dtype=torch.bfloat16, device=dev)
+        self.lg = torch.empty((n, rows, E), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((n, rows, 16), dtype=torch.int32, device=dev)
+        self.wt = torch.empty((n, rows, 16), dtype=torch.float32, device=dev)
+        self.copies = copies
+
+    def run_all(self):
+        r = self.route
+        for i, (w, wr) in enumerate(self.copies):
+            r.fused(self.plan, self.xs[i], w, wr, self.lat[i], self.lg[i], self.ids[i], self.wt[i],
+                    self.ws[i], rows=self.rows)
+
+    def capture(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run_all()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_all()
+        torch.cuda.synchronize()
+        return g
+
+
+def time_graph(g, replays: int, torch):
+    """Average ms per replay of `replays` back-to-back replays (events on the
+    current stream, which is the stream the graph's kernels run on)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / replays
+
+
+def cpu_baseline(rows: int, budget_s: float):
+    """The oracle, as it is, on this host: route_ref_widened on 8-row batches
+    with the weights widened to float64 once outside the timed region."""
+    import numpy as np
+    from oracle import route_oracle as orc
+    from synth import generators as gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    w64, wr64 = orc.widen_weights(gen.latent_weight(0), gen.router_weight(0))
+    banks = [gen.hidden(rows, bank=3000 + b) for b in range(16)]
+    orc.route_ref_widened(banks[0], w64, wr64)      # warm-up
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.route_ref_widened(banks[n % len(banks)], w64, wr64)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 5000:
+            break
+    return {"value": el / n * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} decode routes of {rows} rows (float64 numpy oracle, weights widened "
+                      f"once outside the timed region), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=800, help="timed steps (multiple of 8)")
+    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--rows", type=int, default=8)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--widths", default="1,8,9,12,16,20")
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline width only")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the route computes every row locally and has "
+              "no multi-GPU path to time (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from latent_projection_top_amd import route
+    from synth import generators as gen
+
+    torch.cuda.set_device(0)
+    copies_n = args.copies
+    steps = max(copies_n, (args.steps // copies_n) * copies_n)
+    warm = max(copies_n, (args.warmup // copies_n) * copies_n)
+
+    log(f"generating {copies_n} weight copies ...")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    copies = []
+    for c in range(copies_n):
+        copies.append((bf16(gen.latent_weight(c)), torch.from_numpy(gen.router_weight(c)).cuda()))
+    banks = [bf16(gen.hidden(20, bank=4000 + b)) for b in range(copies_n)]
+
+    results = {}
+    widths = [args.rows] + ([int(w) for w in args.widths.split(",") if int(w) != args.rows]
+                            if not args.no_extras else [])
+    head = None
+    for rows in widths:
+        d = DecodeSetup(rows, copies, banks, route, torch)
+        g = d.capture()
+        reps_w = warm // copies_n
+        for _ in range(reps_w):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = steps // copies_n
+        ms_rep = time_graph(g, reps, torch)
+        us = ms_rep * 1000.0 / copies_n
+        results[rows] = us
+        log(f"decode rows={rows}: {us:.2f} us per route ({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
+        if rows == args.rows:
+            head = (us, ms_rep / copies_n)
+        del g, d
+
+    us8, ms_step = head
+    achieved = decode_bytes(args.rows) / (us8 * 1e-6) / 1e9
+    traffic = committed_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": "decode_route_kernel<1>",
+                "algorithmic_bytes_per_launch": decode_bytes(args.rows)}
+
+    prefill = None
+    if not args.no_extras:
+        rows = 3072
+        plan = route.Plan(route.MODE_PREFILL, rows)
+        ws = plan.new_workspace()
+        x = bf16(gen.hidden(rows, bank=4100, outliers=True))
+        lat = torch.empty((rows, N), dtype=torch.bfloat16, device="cuda")
+        lg = torch.empty((rows, E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((rows, 16), dtype=torch.int32, device="cuda")
+        wt = torch.empty((rows, 16), dtype=torch.float32, device="cuda")
+        w0, wr0 = copies[0]
+
+        def t_call(fn, reps):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            return s.elapsed_time(e) / reps * 1000.0
+
+        t_lr = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
+        t_tk = t_call(lambda: route.topk16(plan, lg, ids, wt), args.prefill_reps)
+        t_all = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
+        gemm_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER_MFMA
+        prefill = {
+            "rows": rows, "us_per_chunk": round(t_all, 2), "rows_per_s": round(rows / (t_all * 1e-6)),
+            "latent_router_us": round(t_lr, 2), "topk16_us": round(t_tk, 2),
+            "mfma_tflops": round(gemm_flops / (t_lr * 1e-6) / 1e12, 1),
+            "mfma_frac": round(gemm_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "router_variant": "bf16x3 split on BF16 MFMA, FP32 runs of 32 folded into FP64",
+        }
+        log(f"prefill 3072: {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
+            f"{t_lr:.1f} us = {prefill['mfma_tflops']} TFLOP/s, top-16 {t_tk:.1f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(args.rows, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.0f} us per route on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(us8, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode route, {args.rows} rows: x[{args.rows},7168] BF16 -> latent "
+                        f"[{args.rows},3584] BF16 + router logits [{args.rows},896] FP32 + "
+                        f"top-16 ids/weights; {copies_n} rotating weight copies "
+                        f"(W[7168,3584] BF16 + Wr[7168,896] FP32, {copies_n * FIXED_BYTES / 1e6:.0f} MB)",
+            "rows": args.rows,
+            "hidden": K, "latent": N, "experts": E, "topk": 16,
+            "weight_copies": copies_n,
+            "timing": "HIP graph of 8 route_fused calls, events on the launch stream",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_us_by_rows": {str(k): round(v, 3) for k, v in sorted(results.items())},
+        "decode_hbm_frac_by_rows": {str(k): round(decode_bytes(k) / (v * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                                    for k, v in sorted(results.items())},
+        "prefill": prefill,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * route.h - C ABI of the per-row MoE route on one AMD Instinct MI355X (gfx950).
+ *
+ * For each token row the route computes
+ *   latent[r, n] = BF16( sum_{k<7168} x[r, k] * W[k, n] ),  n < 3584
+ *       one full-K dot product per output, accumulated in FP32 (partials of
+ *       the K split combined in FP64) and rounded to BF16 once, nearest-even;
+ *       page "Optionally gather the Kimi3 prefill latent instead of reducing
+ *       it" (voipmonitor/flare pull request 16), Description, numerics bullet;
+ *   logits[r, e] = FP32( sum_k x[r, k] * Wr[k, e] ),  e < 896
+ *       FP32 router logits, accumulated in FP64 at decode and in FP32 runs
+ *       folded into FP64 at prefill, rounded once; page "Use two row blocks
+ *       for eight-row Kimi paired gathers" (NVIDIA/hyperflare-inference pull
+ *       request 265) gives the router output as FP32;
+ *   ids[r, 0..15], weights[r, 0..15]
+ *       the standalone top-16: the 16 experts with the largest logits, ordered
+ *       by (logit descending, expert index ascending), -0.0 equal to +0.0, NaN
+ *       below -inf; weights are sigmoid(logit) normalised to sum 1 over the
+ *       16, computed in FP64 and rounded to FP32; page "Kimi K3.1 recipe:
+ *       route 9..20 decode rows through the pushed pair gather and standalone
+ *       top-16" (voipmonitor/flare pull request 24), "What / why" and
+ *       "Dependency".
+ *
+ * Envelope: a plan is prepared once for a mode and a row capacity; decode
+ * plans accept 1..20 rows (the same page, "What / why": rounds of 1..20 rows
+ * are prepared, anything else raises at preparation), prefill plans 1..3072
+ * rows (the 3072-row chunk of pull request 16's timing table). There is no
+ * fallback: every error is a negative status and nothing is launched.
+ *
+ * Ownership and threading:
+ *   - the caller owns every device buffer (inputs, weights, outputs,
+ *     workspace); the library allocates no device memory and never
+ *     synchronises; run calls only enqueue kernels on `stream`, so they can be
+ *     captured into a HIP graph;
+ *   - the workspace (route_workspace_bytes) must be zero-filled once by the
+ *     caller before its first use; every call leaves its counters at zero
+ *     again. Two calls that overlap in time must use different workspaces;
+ *   - a plan is immutable after route_prepare and may be shared by threads.
+ *
+ * Layouts (row-major, all device pointers, 16-byte aligned):
+ *   x        [rows][7168]   BF16 (uint16 bit patterns)
+ *   w_latent [7168][3584]   BF16   ([K][N], N contiguous)
+ *   w_router [7168][896]    FP32   ([K][E], E contiguous)
+ *   latent   [rows][3584]   BF16
+ *   logits   [rows][896]    FP32
+ *   ids      [rows][16]     int32, selection order
+ *   weights  [rows][16]     FP32, same order as ids
+ *
+ * `stream` is a hipStream_t (NULL = the null stream); the current HIP device
+ * must be the plan's device.
+ */
+#ifndef ROUTE_H
+#define ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROUTE_ABI_VERSION 1u
+#define ROUTE_HIDDEN 7168
+#define ROUTE_LATENT 3584
+#define ROUTE_EXPERTS 896
+#define ROUTE_TOPK 16
+#define ROUTE_DECODE_MAX_ROWS 20
+#define ROUTE_PREFILL_MAX_ROWS 3072
+
+/* Status codes. 0 is success; every error is negative and launches nothing. */
+#define ROUTE_OK 0
+#define ROUTE_E_ARG (-1)    /* NULL pointer, bad abi_version or unknown mode */
+#define ROUTE_E_ROWS (-2)   /* rows outside the mode's envelope, or above the plan's */
+#define ROUTE_E_SHAPE (-3)  /* hidden/latent/experts/topk differ from 7168/3584/896/16 */
+#define ROUTE_E_ALIGN (-4)  /* a device pointer is not 16-byte aligned */
+#define ROUTE_E_DEVICE (-5) /* no such device, not gfx950, or not the current device */
+#define ROUTE_E_HIP (-6)    /* the HIP runtime rejected a launch */
+
+typedef enum { ROUTE_MODE_DECODE = 0, ROUTE_MODE_PREFILL = 1 } route_mode;
+
+typedef struct {
+  uint32_t abi_version; /* ROUTE_ABI_VERSION */
+  int32_t mode;         /* route_mode */
+  int32_t rows;         /* the most rows any call on this plan passes */
+  int32_t hidden;       /* 7168 */
+  int32_t latent;       /* 3584 */
+  int32_t experts;      /* 896 */
+  int32_t topk;         /* 16 */
+  int32_t device;       /* HIP device ordinal */
+} route_config;
+
+typedef struct route_plan route_plan; /* opaque, host memory, immutable */
+
+/* Validate cfg and build a plan. Arguments are checked in this order before
+ * any HIP call: cfg/out non-NULL and abi_version (ROUTE_E_ARG), mode
+ * (ROUTE_E_ARG), shape fields (ROUTE_E_SHAPE), rows (ROUTE_E_ROWS); then the
+ * device must exist and be gfx950 (ROUTE_E_DEVICE). On error *out is NULL. */
+int route_prepare(const route_config* cfg, route_plan** out);
+
+/* Bytes of device workspace the plan's run calls need (a multiple of 256;
+ * 0 for a NULL plan). Zero-fill it once before first use. */
+size_t route_workspace_bytes(const route_plan* plan);
+
+/* Latent projection and router logits for `rows` rows (1..plan rows).
+ * Every pointer is required. */
+int route_latent_router(const route_plan* plan, const void* x, const void* w_latent,
+                        const float* w_router, void* latent, float* logits,
+                        void* workspace, int32_t rows, void* stream);
+
+/* Standalone top-16 of `rows` rows of FP32 logits (1..plan rows). */
+int route_topk16(const route_plan* plan, const float* logits, int32_t* ids,
+                 float* weights, int32_t rows, void* stream);
+
+/* The whole route in one call; bitwise equal to route_latent_router followed by
+ * route_topk16 on the same plan. `logits` may be NULL (the logits then live in
+ * the workspace). Decode plans of up to 8 rows select inside the projection
+ * kernel (one launch); wider calls launch the top-16 after it. */
+int route_fused(const route_plan* plan, const void* x, const void* w_latent,
+                const float* w_router, void* latent, float* logits, int32_t* ids,
+                float* weights, void* workspace, int32_t rows, void* stream);
+
+/* Free a plan (NULL is accepted). */
+void route_destroy(route_plan* plan);
+
+/* Static description of a status code. */
+const char* route_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROUTE_H */

@@ -1,0 +1,160 @@
+// C ABI of the route library (libroute.so): plan preparation, argument checks
+// and kernel launches. Every check runs before any launch; nothing allocates
+// device memory or synchronises.
+#include "route.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+
+#include "route_launch.h"
+
+struct route_plan {
+  int32_t mode;
+  int32_t rows_cap;
+  int32_t device;
+  size_t ws_bytes;
+  size_t off_lat;     // decode: latent partials
+  size_t off_rt;      // decode: router partials
+  size_t off_logits;  // logits buffer for route_fused with logits == NULL
+};
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_device(const route_plan* p) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != p->device) return ROUTE_E_DEVICE;
+  return ROUTE_OK;
+}
+
+int check_rows(const route_plan* p, int32_t rows) {
+  return (rows < 1 || rows > p->rows_cap) ? ROUTE_E_ROWS : ROUTE_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? ROUTE_OK : ROUTE_E_HIP; }
+
+route::DecodeWorkspace decode_ws(const route_plan* p, void* ws) {
+  char* base = static_cast<char*>(ws);
+  route::DecodeWorkspace d;
+  d.counters = reinterpret_cast<uint32_t*>(base);
+  d.lat_part = reinterpret_cast<float*>(base + p->off_lat);
+  d.rt_part = reinterpret_cast<double*>(base + p->off_rt);
+  return d;
+}
+
+int run_latent_router(const route_plan* p, const void* x, const void* w_latent, const float* w_router,
+                      void* latent, float* logits, int32_t* ids, float* weights, void* ws,
+                      int32_t rows, bool fused, hipStream_t s) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(w_latent);
+  uint16_t* lb = static_cast<uint16_t*>(latent);
+  if (p->mode == ROUTE_MODE_DECODE) {
+    const bool epilogue = fused && rows <= 8;
+    int st = status_of(route::launch_decode_route(xb, wb, w_router, lb, logits, ids, weights,
+                                                  decode_ws(p, ws), rows, p->rows_cap, epilogue, s));
+    if (st != ROUTE_OK || !fused || epilogue) return st;
+    return status_of(route::launch_topk16(logits, ids, weights, rows, s));
+  }
+  int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, s));
+  if (st != ROUTE_OK) return st;
+  st = status_of(route::launch_prefill_router(xb, w_router, logits, rows, s));
+  if (st != ROUTE_OK || !fused) return st;
+  return status_of(route::launch_topk16(logits, ids, weights, rows, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int route_prepare(const route_config* cfg, route_plan** out) {
+  if (out == nullptr) return ROUTE_E_ARG;
+  *out = nullptr;
+  if (cfg == nullptr || cfg->abi_version != ROUTE_ABI_VERSION) return ROUTE_E_ARG;
+  if (cfg->mode != ROUTE_MODE_DECODE && cfg->mode != ROUTE_MODE_PREFILL) return ROUTE_E_ARG;
+  if (cfg->hidden != ROUTE_HIDDEN || cfg->latent != ROUTE_LATENT || cfg->experts != ROUTE_EXPERTS ||
+      cfg->topk != ROUTE_TOPK)
+    return ROUTE_E_SHAPE;
+  const int32_t max_rows = cfg->mode == ROUTE_MODE_DECODE ? ROUTE_DECODE_MAX_ROWS : ROUTE_PREFILL_MAX_ROWS;
+  if (cfg->rows < 1 || cfg->rows > max_rows) return ROUTE_E_ROWS;
+
+  int count = 0;
+  if (cfg->device < 0 || hipGetDeviceCount(&count) != hipSuccess || cfg->device >= count)
+    return ROUTE_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) return ROUTE_E_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return ROUTE_E_DEVICE;
+
+  route_plan* p = new (std::nothrow) route_plan();
+  if (p == nullptr) return ROUTE_E_ARG;
+  p->mode = cfg->mode;
+  p->rows_cap = cfg->rows;
+  p->device = cfg->device;
+  if (p->mode == ROUTE_MODE_DECODE) {
+    p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, &p->off_lat, &p->off_rt, &p->off_logits);
+  } else {
+    p->off_lat = p->off_rt = 0;
+    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits);
+  }
+  *out = p;
+  return ROUTE_OK;
+}
+
+size_t route_workspace_bytes(const route_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+int route_latent_router(const route_plan* plan, const void* x, const void* w_latent,
+                        const float* w_router, void* latent, float* logits, void* workspace,
+                        int32_t rows, void* stream) {
+  if (!plan || !x || !w_latent || !w_router || !latent || !logits || !workspace) return ROUTE_E_ARG;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(x) || misaligned(w_latent) || misaligned(w_router) || misaligned(latent) ||
+      misaligned(logits) || misaligned(workspace))
+    return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  return run_latent_router(plan, x, w_latent, w_router, latent, logits, nullptr, nullptr, workspace,
+                           rows, false, static_cast<hipStream_t>(stream));
+}
+
+int route_topk16(const route_plan* plan, const float* logits, int32_t* ids, float* weights,
+                 int32_t rows, void* stream) {
+  if (!plan || !logits || !ids || !weights) return ROUTE_E_ARG;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(logits) || misaligned(ids) || misaligned(weights)) return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  return status_of(route::launch_topk16(logits, ids, weights, rows, static_cast<hipStream_t>(stream)));
+}
+
+int route_fused(const route_plan* plan, const void* x, const void* w_latent, const float* w_router,
+                void* latent, float* logits, int32_t* ids, float* weights, void* workspace,
+                int32_t rows, void* stream) {
+  if (!plan || !x || !w_latent || !w_router || !latent || !ids || !weights || !workspace)
+    return ROUTE_E_ARG;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(x) || misaligned(w_latent) || misaligned(w_router) || misaligned(latent) ||
+      (logits && misaligned(logits)) || misaligned(ids) || misaligned(weights) || misaligned(workspace))
+    return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  float* lg = logits ? logits
+                     : reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_logits);
+  return run_latent_router(plan, x, w_latent, w_router, latent, lg, ids, weights, workspace, rows,
+                           true, static_cast<hipStream_t>(stream));
+}
+
+void route_destroy(route_plan* plan) { delete plan; }
+
+const char* route_strerror(int status) {
+  switch (status) {
+    case ROUTE_OK: return "ok";
+    case ROUTE_E_ARG: return "invalid argument (NULL pointer, ABI version or mode)";
+    case ROUTE_E_ROWS: return "row count outside the prepared envelope";
+    case ROUTE_E_SHAPE: return "shape differs from hidden 7168 / latent 3584 / experts 896 / top-16";
+    case ROUTE_E_ALIGN: return "device pointer not 16-byte aligned";
+    case ROUTE_E_DEVICE: return "device missing, not gfx950, or not the current device";
+    case ROUTE_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

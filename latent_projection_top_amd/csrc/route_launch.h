@@ -1,0 +1,34 @@
+// Host-side launchers of the route kernels (called by the C ABI in route_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace route {
+
+// Decode workspace: tile counters, then split-K partials, then a logits buffer.
+struct DecodeWorkspace {
+  uint32_t* counters;  // kDecodeCounters entries, zero between calls
+  float* lat_part;     // [kSplits][rows_cap][3584]
+  double* rt_part;     // [kSplits][rows_cap][896]
+};
+
+size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits);
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits);
+
+hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
+                               uint16_t* latent, float* logits, int32_t* ids, float* weights,
+                               const DecodeWorkspace& ws, int rows, int rows_cap, bool fuse_topk,
+                               hipStream_t stream);
+
+hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,
+                         hipStream_t stream);
+
+hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
+                                 int rows, hipStream_t stream);
+
+hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, float* logits, int rows,
+                                 hipStream_t stream);
+
+}  // namespace route

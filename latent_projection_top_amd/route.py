@@ -1,0 +1,190 @@
+"""Python binding of libroute.so: argument marshalling only.
+
+Each function takes torch tensors (device memory and the current stream are
+torch's), checks dtype, shape and placement so that the C ABI receives the
+pointers it documents, and calls the C entry point of the same name. Every step
+of the route runs in the library's HIP kernels. A non-zero status raises
+RouteError; there is no fallback of any kind. If libroute.so is missing the
+import of this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HIDDEN = 7168
+LATENT = 3584
+EXPERTS = 896
+TOPK = 16
+DECODE_MAX_ROWS = 20
+PREFILL_MAX_ROWS = 3072
+ABI_VERSION = 1
+MODE_DECODE = 0
+MODE_PREFILL = 1
+
+OK = 0
+E_ARG = -1
+E_ROWS = -2
+E_SHAPE = -3
+E_ALIGN = -4
+E_DEVICE = -5
+E_HIP = -6
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libroute.so")
+
+SYMBOLS = ("route_prepare", "route_workspace_bytes", "route_latent_router", "route_topk16",
+           "route_fused", "route_destroy", "route_strerror")
+
+
+class RouteError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class RouteConfig(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("mode", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("latent", ctypes.c_int32), ("experts", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("device", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32p, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+    lib.route_prepare.argtypes = [ctypes.POINTER(RouteConfig), ctypes.POINTER(ctypes.c_void_p)]
+    lib.route_prepare.restype = ctypes.c_int
+    lib.route_workspace_bytes.argtypes = [vp]
+    lib.route_workspace_bytes.restype = ctypes.c_size_t
+    lib.route_latent_router.argtypes = [vp, vp, vp, f32p, vp, f32p, vp, i32, vp]
+    lib.route_latent_router.restype = ctypes.c_int
+    lib.route_topk16.argtypes = [vp, f32p, i32p, f32p, i32, vp]
+    lib.route_topk16.restype = ctypes.c_int
+    lib.route_fused.argtypes = [vp, vp, vp, f32p, vp, f32p, i32p, f32p, vp, i32, vp]
+    lib.route_fused.restype = ctypes.c_int
+    lib.route_destroy.argtypes = [vp]
+    lib.route_destroy.restype = None
+    lib.route_strerror.argtypes = [ctypes.c_int]
+    lib.route_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def strerror(status: int) -> str:
+    return LIB.route_strerror(int(status)).decode()
+
+
+def make_config(mode: int, rows: int, device: int = 0, hidden: int = HIDDEN,
+                latent: int = LATENT, experts: int = EXPERTS, topk: int = TOPK,
+                abi_version: int = ABI_VERSION) -> RouteConfig:
+    return RouteConfig(abi_version, mode, rows, hidden, latent, experts, topk, device)
+
+
+def prepare_raw(cfg) -> tuple[int, int]:
+    """Call route_prepare; returns (status, plan handle or 0). cfg may be None."""
+    out = ctypes.c_void_p(0)
+    st = LIB.route_prepare(ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out))
+    return st, (out.value or 0)
+
+
+class Plan:
+    """A prepared route plan (owns the C plan; freed on close/GC)."""
+
+    def __init__(self, mode: int, rows: int, device: int | None = None):
+        if device is None:
+            device = torch.cuda.current_device()
+        st, handle = prepare_raw(make_config(mode, rows, device))
+        if st != OK:
+            raise RouteError(st, "route_prepare")
+        self.handle = handle
+        self.mode = mode
+        self.rows = rows
+        self.device = device
+        self.workspace_bytes = int(LIB.route_workspace_bytes(ctypes.c_void_p(handle)))
+
+    def new_workspace(self) -> torch.Tensor:
+        """A zero-filled workspace tensor of the size this plan needs."""
+        return torch.zeros(max(self.workspace_bytes, 16), dtype=torch.uint8,
+                           device=f"cuda:{self.device}")
+
+    def close(self):
+        if getattr(self, "handle", 0):
+            LIB.route_destroy(ctypes.c_void_p(self.handle))
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr(t: torch.Tensor | None, dtype, shape=None, name: str = "") -> int | None:
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+    if shape is not None and tuple(t.shape[1:]) != tuple(shape[1:]):
+        raise ValueError(f"{name}: expected trailing shape {shape[1:]}, got {tuple(t.shape)}")
+    if shape is not None and t.shape[0] < shape[0]:
+        raise ValueError(f"{name}: needs at least {shape[0]} rows, has {t.shape[0]}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream or None
+
+
+def latent_router(plan: Plan, x, w_latent, w_router, latent, logits, workspace,
+                  rows: int | None = None, stream=None) -> None:
+    rows = x.shape[0] if rows is None else rows
+    st = LIB.route_latent_router(
+        ctypes.c_void_p(plan.handle),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent"),
+        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router"),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_latent_router")
+
+
+def topk16(plan: Plan, logits, ids, weights, rows: int | None = None, stream=None) -> None:
+    rows = logits.shape[0] if rows is None else rows
+    st = LIB.route_topk16(
+        ctypes.c_void_p(plan.handle),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_topk16")
+
+
+def fused(plan: Plan, x, w_latent, w_router, latent, logits, ids, weights, workspace,
+          rows: int | None = None, stream=None) -> None:
+    rows = x.shape[0] if rows is None else rows
+    st = LIB.route_fused(
+        ctypes.c_void_p(plan.handle),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent"),
+        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router"),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_fused")

@@ -78,6 +78,32 @@ def latent_check(got_bits, ref_bits, exact, abs_terms) -> dict:
     }
 
 
+def f32_spacing(v: np.ndarray) -> np.ndarray:
+    """float32 unit in the last place at each float32 value."""
+    e = (np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.int64) >> 23) & 0xFF
+    return np.ldexp(1.0, np.where(e == 0, -149, e - 127 - 23))
+
+
+def logits_check(got, ref, exact, abs_terms, c: float = 1.0) -> dict:
+    """Judge FP32 logits: within 1 ULP of the correctly rounded value, or
+    |got - exact| <= ulp(got)/2 + c * 2**-24 * sum_k |x_k Wr_k| (the error any
+    summation of FP32-rounded partial sums can reach when a logit is small
+    against the magnitude of its terms)."""
+    got = np.asarray(got, dtype=np.float32)
+    d = f32_ulp_distance(got, ref)
+    within = d <= 1
+    err = np.abs(got.astype(np.float64) - exact)
+    band_ok = err <= 0.5 * f32_spacing(got) + c * U32 * abs_terms
+    return {
+        "n": int(d.size),
+        "within_1ulp": int(within.sum()),
+        "band": int(((~within) & band_ok).sum()),
+        "fail": int(((~within) & (~band_ok)).sum()),
+        "max_ulp": int(d.max()) if d.size else 0,
+        "max_err_over_terms": float((err / (U32 * abs_terms)).max()) if d.size else 0.0,
+    }
+
+
 def ids_check(got_ids, ref_ids, ref_logits, max_ulp: int = 2) -> dict:
     """End-to-end id rule. Returns counts of equal rows, 1-for-1 swap rows and
     violating rows (with the violating row indices)."""

@@ -190,13 +190,26 @@ def route_weights_ref(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------- whole route --
 
-def route_ref(x_bits: np.ndarray, w_bits: np.ndarray, w_router: np.ndarray) -> dict:
-    """Every output of the route for the given rows."""
-    logits = logits_ref(x_bits, w_router)
+def widen_weights(w_bits: np.ndarray, w_router: np.ndarray):
+    """float64 copies of the latent and router weights (exact widening), so a
+    caller routing many batches through the same layer converts them once."""
+    return bf16_bits_to_f64(w_bits), np.asarray(w_router, dtype=np.float32).astype(np.float64)
+
+
+def route_ref_widened(x_bits: np.ndarray, w64: np.ndarray, wr64: np.ndarray) -> dict:
+    """Every output of the route, from weights already widened to float64.
+    The same steps as latent_ref, logits_ref, topk16_ref and route_weights_ref."""
+    x = bf16_bits_to_f64(x_bits)
+    logits = (x @ wr64).astype(np.float32)
     ids = topk16_ref(logits)
     return {
-        "latent": latent_ref(x_bits, w_bits),
+        "latent": round_f64_to_bf16_bits(x @ w64),
         "logits": logits,
         "ids": ids,
         "weights": route_weights_ref(logits, ids),
     }
+
+
+def route_ref(x_bits: np.ndarray, w_bits: np.ndarray, w_router: np.ndarray) -> dict:
+    """Every output of the route for the given rows."""
+    return route_ref_widened(x_bits, *widen_weights(w_bits, w_router))

@@ -1,0 +1,85 @@
+"""GPU parity of the prefill route (up to 3072 rows) through the C ABI.
+
+Workload: 3072-row chunks (page "Optionally gather the Kimi3 prefill latent
+instead of reducing it", timing table) with 1 % of hidden channels scaled x20
+as outliers. At this size the float64 oracle still runs on the host in
+seconds, so every output is compared, for several banks; ragged row counts
+check the M tail of the tiles."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import compare
+from oracle import route_oracle as orc
+from synth import generators as gen
+from tests.routekit import Outputs, bf16_dev, log, oracle_rows, weights_dev
+
+pytestmark = pytest.mark.gpu
+
+route = pytest.importorskip("latent_projection_top_amd.route")
+
+
+def run_prefill(x_bits, cap=3072, fused=False):
+    w, wr = weights_dev(0)
+    rows = x_bits.shape[0]
+    plan = route.Plan(route.MODE_PREFILL, cap)
+    ws = plan.new_workspace()
+    xd = bf16_dev(x_bits)
+    out = Outputs(rows)
+    out.poison()
+    if fused:
+        route.fused(plan, xd, w, wr, out.latent, out.logits, out.ids, out.weights, ws, rows=rows)
+    else:
+        route.latent_router(plan, xd, w, wr, out.latent, out.logits, ws, rows=rows)
+        route.topk16(plan, out.logits, out.ids, out.weights, rows=rows)
+    torch.cuda.synchronize()
+    return out.host()
+
+
+def judge(xs, got, tag):
+    ref = oracle_rows(xs)
+    lc = compare.latent_check(got["latent"], ref["latent"], ref["exact"], ref["abs_terms"])
+    gc = compare.logits_check(got["logits"], ref["logits"], ref["logits_exact"],
+                              ref["logits_abs_terms"])
+    ld = compare.f32_ulp_distance(got["logits"], ref["logits"])
+    top = np.abs(ref["logits_exact"]) >= 1.0
+    ic = compare.ids_check(got["ids"], ref["ids"], ref["logits"])
+    wc = compare.weights_check(got["weights"], orc.route_weights_ref(got["logits"], got["ids"]))
+    same = (got["ids"] == ref["ids"]).all(axis=1)
+    wc2 = compare.weights_check(got["weights"][same], ref["weights"][same])
+    log(f"{tag}: latent {lc} | logits {gc}, |l|>=1 ulp max {ld[top].max()} mean "
+        f"{ld[top].mean():.3g} | ids equal {ic['equal']} swaps {ic['swaps']} viol "
+        f"{ic['violations']} | weights max {wc['max_ulp']} / e2e {wc2['max_ulp']}")
+    assert lc["fail"] == 0
+    assert lc["rel_rms"] <= 2.0e-3
+    assert lc["band"] <= max(4, 1e-4 * lc["n"])
+    assert gc["fail"] == 0
+    assert ic["violations"] == 0, ic["bad_rows"][:5]
+    assert wc["fail"] == 0 and wc2["fail"] == 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bank", [0, 1, 2, 3])
+def test_prefill_chunk_3072_outliers(bank):
+    log(f"prefill 3072 rows, outliers, bank={bank}")
+    xs = gen.hidden(3072, bank=500 + bank, outliers=True)
+    got = run_prefill(xs, fused=(bank % 2 == 1))
+    judge(xs, got, f"prefill 3072 bank {bank}")
+
+
+@pytest.mark.parametrize("rows", [1, 77, 130, 1000])
+def test_prefill_ragged(rows):
+    log(f"prefill ragged rows={rows}")
+    xs = gen.hidden(rows, bank=600 + rows, outliers=True)
+    got = run_prefill(xs, cap=3072)
+    judge(xs, got, f"prefill rows={rows}")
+
+
+def test_prefill_fused_equals_two_calls():
+    log("prefill fused == two calls")
+    xs = gen.hidden(300, bank=9)
+    a = run_prefill(xs, cap=512, fused=True)
+    b = run_prefill(xs, cap=512, fused=False)
+    for k in ("latent", "logits", "ids"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["weights"].view(np.uint32), b["weights"].view(np.uint32))

@@ -377,3 +377,12 @@ def test_ids_check_rules():
     outside = [i for i in range(g.EXPERTS) if i not in set(ids[0].tolist())][0]
     swapped[0, 15] = outside
     assert c.ids_check(swapped, ids, L)["violations"] == 1
+
+
+def test_route_ref_widened_matches_parts():
+    x = g.hidden(3, bank=11)
+    w, wr = g.latent_weight(0), g.router_weight(0)
+    a = o.route_ref(x, w, wr)
+    assert np.array_equal(a["latent"], o.latent_ref(x, w))
+    assert np.array_equal(a["logits"], o.logits_ref(x, wr))
+    assert np.array_equal(a["ids"], o.topk16_ref(o.logits_ref(x, wr)))
