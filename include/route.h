@@ -113,8 +113,8 @@ int route_topk16(const route_plan* plan, const float* logits, int32_t* ids,
 
 /* The whole route in one call; bitwise equal to route_latent_router followed by
  * route_topk16 on the same plan. `logits` may be NULL (the logits then live in
- * the workspace). Decode plans of up to 8 rows select inside the projection
- * kernel (one launch); wider calls launch the top-16 after it. */
+ * the workspace). Decode plans select inside the projection kernel (one
+ * launch); prefill plans launch the top-16 after the two GEMMs. */
 int route_fused(const route_plan* plan, const void* x, const void* w_latent,
                 const float* w_router, void* latent, float* logits, int32_t* ids,
                 float* weights, void* workspace, int32_t rows, void* stream);

@@ -1,61 +1,98 @@
-// Decode route (1..20 rows): latent down projection + FP32 router logits in one
-// weight-streaming, split-K kernel, with the standalone top-16 optionally
-// fused into its epilogue.
+// Decode route (1..20 rows): latent down projection + FP32 router logits +
+// standalone top-16 in one weight-streaming kernel.
 //
 // What is computed (page "Optionally gather the Kimi3 prefill latent instead of
 // reducing it", voipmonitor/flare pull request 16, Description, numerics
 // bullet): every latent value is one FP32-accumulated dot product over the
-// full K = 7168, rounded to BF16 once. On one GPU there is no exchange: the K
-// range is split S = 8 ways only to spread the 77 MB of weights over all
-// compute units, and the S partials are combined in FP64 in a fixed order
-// before the single rounding.
+// full K = 7168, rounded to BF16 once. On one GPU there is no exchange: K is
+// split only to spread the 77 MB of weights over all compute units, and the
+// partials are combined in FP64 in a fixed order before the single rounding.
+// The router logits are FP32 (page "Use two row blocks for eight-row Kimi
+// paired gathers", NVIDIA/hyperflare-inference pull request 265); each row's
+// experts are chosen by the standalone top-16 (page "Kimi K3.1 recipe: route
+// 9..20 decode rows through the pushed pair gather and standalone top-16",
+// voipmonitor/flare pull request 24, "What / why").
 //
-// Shape of the work (all constants, K = 7168, N = 3584, E = 896):
-//   latent blocks: 56 column tiles of 64 x 8 K-splits of 896 rows = 448 blocks
-//   router blocks: 28 expert tiles of 32 x 8 K-splits of 896 rows = 224 blocks
-// Every block streams the same 114,688 bytes of weight (896 rows x 128 bytes),
-// so the 672 blocks finish together. Four waves per block take 224 rows each.
+// Work split: 672 workgroups of 4 waves, all resident at once.
+//   workgroups 0..447, dispatched first: router units, expert tile (32
+//       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
+//       bytes) of the FP32 router weight and the unit stores one FP64 partial
+//       per (row, expert); the last unit of a tile sums the 16 partials;
+//   workgroups 448..671: latent units, column tile (64 columns) x K chunk of
+//       1792 rows; each wave streams 448 rows (57,344 bytes) of the BF16 latent
+//       weight; the last unit of a tile sums the 4 partials and rounds once.
+// Router waves have a quarter of a latent wave's bytes and finish early; the
+// workgroup that combines the last router tile then selects the top-16 of
+// every row, four rows at a time (one per wave), while the latent weight is
+// still streaming, and latent workgroups take any rows left when they finish. Nothing ever waits for another workgroup; every unit's arithmetic
+// and combine order is fixed, so results do not depend on scheduling.
 //
-// Latent, per wave and 32-row step: each lane reads 8 rows x 4 columns
+// Latent unit, per wave and 32-row step: each lane reads 8 rows x 4 columns
 // (8-byte loads; 16 lanes cover one 128-byte row segment), transposes the 8x4
 // BF16 block in registers with v_perm so that each of 4 registers holds 8
-// consecutive-K values of one column, and issues 4 (or 8 for 17..20 rows)
-// v_mfma_f32_16x16x32_bf16 with the hidden rows as the 16-wide N side. The MFMA
-// accumulates in FP32. Rows are padded to 16 (32) inside the MFMA only.
+// consecutive-K values of one column, and issues 4 (8 for 17..20 rows)
+// v_mfma_f32_16x16x32_bf16 with the hidden rows on the N side (padded to 16 or
+// 32 inside the MFMA only). FP32 accumulation; the unit's 4 waves are summed in
+// FP64; the last unit of a tile sums the 4 partials in FP64 and rounds once.
 //
-// Router, per wave: v_mfma_f64_16x16x4_f64 with FP32 weights widened to FP64
-// (exact) and BF16 hidden values widened to FP64 (exact): the logits are
-// accumulated in FP64 end to end and rounded to FP32 once.
-//
-// Split-K combine: each block sums its 4 waves (FP64, fixed order) and stores
-// one partial per output (latent: FP32, router: FP64). The last of a tile's 8
-// blocks (integer counter, release/acquire fences) sums the 8 partials in FP64
-// in split order, rounds once, writes the output and resets the counter. With
-// fuse_topk the last router tile to finish then runs the top-16 for every row.
+// Router unit, per wave and 16-row step: v_mfma_f64_16x16x4_f64 with the FP32
+// weights and the BF16 hidden values widened exactly to FP64, so the logits
+// are accumulated in FP64 end to end and rounded to FP32 once.
 #include "route_device.h"
 #include "route_launch.h"
 
 namespace route {
 
-constexpr int kSplits = 8;
-constexpr int kKSplit = kHidden / kSplits;           // 896
 constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;             // 256
-constexpr int kKWave = kKSplit / kWaves;             // 224
-constexpr int kStep = 32;
-constexpr int kStepsPerWave = kKWave / kStep;        // 7
-constexpr int kLatTileN = 64;
-constexpr int kLatTiles = kLatent / kLatTileN;       // 56
-constexpr int kRtTileE = 32;
-constexpr int kRtTiles = kExperts / kRtTileE;        // 28
-constexpr int kLatBlocks = kLatTiles * kSplits;      // 448
-constexpr int kRtBlocks = kRtTiles * kSplits;        // 224
-constexpr int kDecodeBlocks = kLatBlocks + kRtBlocks;
-constexpr int kDecodeCounters = kLatTiles + kRtTiles + 1;
-constexpr int kDecodeMaxRows = 20;
+constexpr int kThreads = kWaves * kWave;              // 256
 
-static_assert(kHidden % (kSplits * kWaves * kStep) == 0, "K split");
+// latent units
+constexpr int kSplitsL = 4;
+constexpr int kKL = kHidden / kSplitsL;               // 1792 rows per unit
+constexpr int kKLWave = kKL / kWaves;                 // 448 rows per wave
+constexpr int kStepL = 32;
+constexpr int kStepsL = kKLWave / kStepL;             // 14
+constexpr int kLatTileN = 64;
+constexpr int kLatTiles = kLatent / kLatTileN;        // 56
+constexpr int kLatUnits = kLatTiles * kSplitsL;       // 224
+
+// router units
+constexpr int kSplitsR = 16;
+constexpr int kKR = kHidden / kSplitsR;               // 448 rows per unit
+constexpr int kKRWave = kKR / kWaves;                 // 112 rows per wave
+constexpr int kStepR = 16;
+constexpr int kStepsR = kKRWave / kStepR;             // 7
+constexpr int kRtTileE = 32;
+constexpr int kRtTiles = kExperts / kRtTileE;         // 28
+constexpr int kRtUnits = kRtTiles * kSplitsR;         // 448
+
+constexpr int kGrid = kRtUnits + kLatUnits;           // 672: one workgroup per unit
+constexpr int kDecodeMaxRows = 20;
+constexpr int kRowGroup = kWaves;                     // rows selected together, one per wave
+
+// Workspace counters (uint32). Every counter is shared by few workgroups:
+// atomics on one address from hundreds of workgroups serialise.
+constexpr int kCtrRtTile = kLatTiles;                 // [28] router units stored per tile
+constexpr int kCtrRouter = kLatTiles + kRtTiles;      // router tiles combined
+constexpr int kCtrRows = kCtrRouter + 1;              // rows claimed
+constexpr int kCtrFin = kCtrRouter + 2;               // row-phase participants finished
+constexpr int kDecodeCounters = kCtrRouter + 3;
+// Row-phase participants: the workgroup that combines the last router tile and
+// the 56 workgroups that combine a latent tile, each exactly once per call.
+constexpr int kRowParticipants = 1 + kLatTiles;
+
+static_assert(kKLWave % kStepL == 0 && kKRWave % kStepR == 0, "whole steps per wave");
 static_assert(kLatent % kLatTileN == 0 && kExperts % kRtTileE == 0, "tiles");
+
+// Rows a workgroup keeps in its LDS reduction buffer: the MFMA pads rows to 16
+// or 32, but only real rows (at most 20) are stored.
+template <int NT>
+constexpr int rows_kept() { return NT == 1 ? 16 : kDecodeMaxRows; }
+
+// Latent steps of loads kept in flight per wave (fewer at 17..20 rows, where
+// the second set of hidden-row fragments and accumulators needs registers).
+template <int NT>
+constexpr int depth() { return NT == 1 ? 4 : 3; }
 
 struct DecodeArgs {
   const uint16_t* __restrict__ x;
@@ -65,8 +102,8 @@ struct DecodeArgs {
   float* __restrict__ logits;
   int32_t* __restrict__ ids;
   float* __restrict__ weights;
-  float* __restrict__ lat_part;
-  double* __restrict__ rt_part;
+  float* __restrict__ lat_part;   // [kSplitsL][rows_cap][N]
+  double* __restrict__ rt_part;   // [kSplitsR][rows_cap][E]
   uint32_t* __restrict__ counters;
   int rows;
   int rows_cap;
@@ -76,9 +113,9 @@ struct DecodeArgs {
 // Cross-workgroup handoff without device-wide cache maintenance. Each XCD has
 // its own L2 and a device-scope fence would write back and invalidate the whole
 // L2 for every workgroup. Instead, everything one workgroup hands to another
-// (partials, logits for the fused select, counters) moves through device-scope
-// relaxed atomic stores and loads, which the compiler emits with the sc1 bit so
-// that they are coherent across XCDs; a store is complete once vmcnt drains.
+// (partials, counters) moves through device-scope relaxed atomic stores and
+// loads, which the compiler emits with the sc1 bit so that they are coherent
+// across XCDs; a store is complete once vmcnt drains.
 template <typename T>
 __device__ __forceinline__ void st_dev(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -86,6 +123,9 @@ __device__ __forceinline__ void st_dev(T* p, T v) {
 template <typename T>
 __device__ __forceinline__ T ld_dev(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until this thread's outstanding vector memory operations (stores
@@ -96,174 +136,104 @@ __device__ __forceinline__ void drain_vmem() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// True in the workgroup that arrives last of `expected`. Every thread's st_dev
-// stores are complete before thread 0 bumps the counter, so the last workgroup
-// reads all of them with ld_dev.
-__device__ __forceinline__ bool last_arrival(uint32_t* counter, int expected, int* flag) {
+// Broadcast thread 0's value to the workgroup.
+__device__ __forceinline__ int broadcast(int v, int* slot) {
+  if (threadIdx.x == 0) *slot = v;
+  __syncthreads();
+  const int r = *slot;
+  __syncthreads();
+  return r;
+}
+
+// All threads' st_dev stores complete, then thread 0 adds 1 to `counter`;
+// every thread gets the previous value.
+__device__ __forceinline__ uint32_t publish(uint32_t* counter, int* slot) {
   drain_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (prev == (uint32_t)(expected - 1));
-  }
-  __syncthreads();
-  return *flag != 0;
+  int prev = 0;
+  if (threadIdx.x == 0) prev = (int)add_dev(counter, 1u);
+  return (uint32_t)broadcast(prev, slot);
 }
 
+// MFMA output column r only depends on hidden row r, and columns r >= rows are
+// never stored, so padding lanes load a valid row (the last) without a branch:
+// a branch here would drain the weight loads in flight at its join.
 template <int NT>
-__device__ void latent_block(const DecodeArgs& a, int b, float* red, int* flag) {
-  const int tile = b % kLatTiles;
-  const int split = b / kLatTiles;
+__device__ __forceinline__ void hidden_rows(const DecodeArgs& a, int m, int (&xr)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) xr[nt] = min(16 * nt + m, a.rows - 1);
+}
+
+// Returns true in the workgroup that combined the last router tile: every
+// logit of every row is then stored.
+template <int NT>
+__device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int m = lane & 15;
-  const int n0 = tile * kLatTileN;
-  const int k0 = split * kKSplit + wave * kKWave;
+  constexpr int kRowsPad = rows_kept<NT>();
+  int xr[NT];
+  hidden_rows<NT>(a, m, xr);
 
-  f32x4 acc[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint16_t* wp = a.w + (size_t)(k0 + 8 * g) * kLatent + n0 + 4 * m;
-  const uint16_t* xp[NT];
-  bool xok[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = 16 * nt + m;
-    xok[nt] = r < a.rows;
-    xp[nt] = a.x + (size_t)(xok[nt] ? r : 0) * kHidden + k0 + 8 * g;
-  }
-
-#pragma unroll
-  for (int st = 0; st < kStepsPerWave; ++st) {
-    u32x2 wv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wv[j] = __builtin_nontemporal_load((const u32x2*)(wp + (size_t)(st * kStep + j) * kLatent));
-    u32x4 xv[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      xv[nt] = xok[nt] ? *(const u32x4*)(xp[nt] + st * kStep) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 av;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        av[p] = __builtin_amdgcn_perm(wv[2 * p + 1][c >> 1], wv[2 * p][c >> 1], sel);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv[nt]), acc[nt][c], 0, 0, 0);
-    }
-  }
-
-  // lane (g, m) holds row 16*nt + m, local columns 16*g + 4*t + c
-  constexpr int kRowsPad = 16 * NT;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        red[(wave * kRowsPad + 16 * nt + m) * kLatTileN + 16 * g + 4 * t + c] = acc[nt][c][t];
-  __syncthreads();
-
-  const int outs = a.rows * kLatTileN;
-  for (int i = threadIdx.x; i < outs; i += kThreads) {
-    const int r = i / kLatTileN;
-    const int col = i % kLatTileN;
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += (double)red[(w * kRowsPad + r) * kLatTileN + col];
-    st_dev(&a.lat_part[((size_t)split * a.rows_cap + r) * kLatent + n0 + col], (float)s);
-  }
-
-  if (!last_arrival(&a.counters[tile], kSplits, flag)) return;
-
-  for (int i = threadIdx.x; i < outs; i += kThreads) {
-    const int r = i / kLatTileN;
-    const int col = i % kLatTileN;
-    double s = 0.0;
-#pragma unroll
-    for (int sp = 0; sp < kSplits; ++sp)
-      s += (double)ld_dev(&a.lat_part[((size_t)sp * a.rows_cap + r) * kLatent + n0 + col]);
-    a.latent[(size_t)r * kLatent + n0 + col] = f64_to_bf16_rne(s);
-  }
-  if (threadIdx.x == 0) st_dev(&a.counters[tile], 0u);
-}
-
-template <int NT>
-__device__ void router_block(const DecodeArgs& a, int b, double* red, int* flag) {
-  const int tile = b % kRtTiles;
-  const int split = b / kRtTiles;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  const int m = lane & 15;
+  const int tile = u % kRtTiles;
+  const int split = u / kRtTiles;
   const int e0 = tile * kRtTileE;
-  const int k0 = split * kKSplit + wave * kKWave;
+  const int k0 = split * kKR + wave * kKRWave;
+  const float* wp = a.wr + (size_t)(k0 + 4 * g) * kExperts + e0 + 2 * m;
 
   f64x4 acc[NT][2];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 2; ++c) acc[nt][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-
-  const float* wp = a.wr + (size_t)(k0 + 8 * g) * kExperts + e0 + 2 * m;
-  const uint16_t* xp[NT];
-  bool xok[NT];
+  constexpr int kDepthR = 4;
+  f32x2 wv[kDepthR][4];
+  u32x2 xv[kDepthR][NT];
+  auto issue = [&](int st) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = 16 * nt + m;
-    xok[nt] = r < a.rows;
-    xp[nt] = a.x + (size_t)(xok[nt] ? r : 0) * kHidden + k0 + 8 * g;
-  }
-
-#pragma unroll 1
-  for (int st = 0; st < kStepsPerWave; ++st) {
-    f32x2 wv[8];
+    for (int j = 0; j < 4; ++j)
+      wv[st % kDepthR][j] =
+          __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStepR + j) * kExperts));
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wv[j] = __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStep + j) * kExperts));
-    double xd[NT][8];
+    for (int nt = 0; nt < NT; ++nt)
+      xv[st % kDepthR][nt] = *(const u32x2*)(a.x + (size_t)xr[nt] * kHidden + k0 + 4 * g + st * kStepR);
+  };
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const u32x4 xv = xok[nt] ? *(const u32x4*)(xp[nt] + st * kStep) : u32x4{0u, 0u, 0u, 0u};
+  for (int st = 0; st < kDepthR; ++st) issue(st);
+  __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        xd[nt][2 * p] = (double)bf16_lo(xv[p]);
-        xd[nt][2 * p + 1] = (double)bf16_hi(xv[p]);
-      }
-    }
+  for (int st = 0; st < kStepsR; ++st) {
+    const int q = st % kDepthR;
+    // lane (g, m) at step j: A[m][g] = Wr[k][e0 + 2m + c], B[g][m] = x[row m][k],
+    // k = k0 + 16*st + 4*g + j
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double w0 = (double)wv[j][0];
-      const double w1 = (double)wv[j][1];
+    for (int j = 0; j < 4; ++j) {
+      const double w0 = (double)wv[q][j][0];
+      const double w1 = (double)wv[q][j][1];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(w0, xd[nt][j], acc[nt][0], 0, 0, 0);
-        acc[nt][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w1, xd[nt][j], acc[nt][1], 0, 0, 0);
+        const double xd = (double)((j & 1) ? bf16_hi(xv[q][nt][j >> 1]) : bf16_lo(xv[q][nt][j >> 1]));
+        acc[nt][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(w0, xd, acc[nt][0], 0, 0, 0);
+        acc[nt][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w1, xd, acc[nt][1], 0, 0, 0);
       }
     }
+    if (st + kDepthR < kStepsR) issue(st + kDepthR);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
+  double* red = reinterpret_cast<double*>(smem);
   // The FP64 MFMA keeps D[4*t + g][m] in slot t of lane (g, m): lane (g, m)
   // holds row 16*nt + m, local experts 2*(4*t + g) + c = 8*t + 2*g + c.
-  constexpr int kRowsPad = 16 * NT;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        red[(wave * kRowsPad + 16 * nt + m) * kRtTileE + 8 * t + 2 * g + c] = acc[nt][c][t];
+        if (16 * nt + m < kRowsPad)
+          red[(wave * kRowsPad + 16 * nt + m) * kRtTileE + 8 * t + 2 * g + c] = acc[nt][c][t];
   __syncthreads();
-
   const int outs = a.rows * kRtTileE;
   for (int i = threadIdx.x; i < outs; i += kThreads) {
     const int r = i / kRtTileE;
@@ -273,40 +243,178 @@ __device__ void router_block(const DecodeArgs& a, int b, double* red, int* flag)
     for (int w = 0; w < kWaves; ++w) s += red[(w * kRowsPad + r) * kRtTileE + e];
     st_dev(&a.rt_part[((size_t)split * a.rows_cap + r) * kExperts + e0 + e], s);
   }
-
-  if (!last_arrival(&a.counters[kLatTiles + tile], kSplits, flag)) return;
-
+  if (publish(&a.counters[kCtrRtTile + tile], slot) != (uint32_t)(kSplitsR - 1)) return false;
+  // last unit of this tile: the tile's logits from its 16 partials
   for (int i = threadIdx.x; i < outs; i += kThreads) {
     const int r = i / kRtTileE;
     const int e = i % kRtTileE;
+    double p[kSplitsR];
+#pragma unroll
+    for (int sp = 0; sp < kSplitsR; ++sp)
+      p[sp] = ld_dev(&a.rt_part[((size_t)sp * a.rows_cap + r) * kExperts + e0 + e]);
     double s = 0.0;
 #pragma unroll
-    for (int sp = 0; sp < kSplits; ++sp) s += ld_dev(&a.rt_part[((size_t)sp * a.rows_cap + r) * kExperts + e0 + e]);
+    for (int sp = 0; sp < kSplitsR; ++sp) s += p[sp];
     st_dev(&a.logits[(size_t)r * kExperts + e0 + e], (float)s);
   }
-  if (threadIdx.x == 0) st_dev(&a.counters[kLatTiles + tile], 0u);
-
-  if (!a.fuse_topk) return;
-  uint32_t* done = &a.counters[kLatTiles + kRtTiles];
-  if (!last_arrival(done, kRtTiles, flag)) return;
-  for (int r = wave; r < a.rows; r += kWaves)
-    topk16_wave<true>(a.logits + (size_t)r * kExperts, a.ids + (size_t)r * kTopK,
-                      a.weights + (size_t)r * kTopK);
-  if (threadIdx.x == 0) st_dev(done, 0u);
+  if (threadIdx.x == 0) st_dev(&a.counters[kCtrRtTile + tile], 0u);
+  return publish(&a.counters[kCtrRouter], slot) == (uint32_t)(kRtTiles - 1);
 }
 
 template <int NT>
-__global__ __launch_bounds__(kThreads) void decode_route_kernel(DecodeArgs a) {
-  constexpr int kLatBytes = kWaves * 16 * NT * kLatTileN * 4;
-  constexpr int kRtBytes = kWaves * 16 * NT * kRtTileE * 8;
-  constexpr int kBytes = kLatBytes > kRtBytes ? kLatBytes : kRtBytes;
+__device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int m = lane & 15;
+  constexpr int kRowsPad = rows_kept<NT>();
+  int xr[NT];
+  hidden_rows<NT>(a, m, xr);
+
+  const int tile = u % kLatTiles;
+  const int split = u / kLatTiles;
+  const int n0 = tile * kLatTileN;
+  const int k0 = split * kKL + wave * kKLWave;
+  const uint16_t* wp = a.w + (size_t)(k0 + 8 * g) * kLatent + n0 + 4 * m;
+
+  f32x4 acc[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kDepth = depth<NT>();
+  u32x2 wv[kDepth][8];
+  u32x4 xv[kDepth][NT];
+  auto issue = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wv[st % kDepth][j] =
+          __builtin_nontemporal_load((const u32x2*)(wp + (size_t)(st * kStepL + j) * kLatent));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      xv[st % kDepth][nt] = *(const u32x4*)(a.x + (size_t)xr[nt] * kHidden + k0 + 8 * g + st * kStepL);
+  };
+#pragma unroll
+  for (int st = 0; st < kDepth; ++st) issue(st);
+  __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
+#pragma unroll
+  for (int st = 0; st < kStepsL; ++st) {
+    const int q = st % kDepth;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 av;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        av[p] = __builtin_amdgcn_perm(wv[q][2 * p + 1][c >> 1], wv[q][2 * p][c >> 1], sel);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv[q][nt]), acc[nt][c], 0, 0, 0);
+    }
+    if (st + kDepth < kStepsL) issue(st + kDepth);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  float* red = reinterpret_cast<float*>(smem);
+  // lane (g, m) holds row 16*nt + m, local columns 16*g + 4*t + c
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (16 * nt + m < kRowsPad)
+          red[(wave * kRowsPad + 16 * nt + m) * kLatTileN + 16 * g + 4 * t + c] = acc[nt][c][t];
+  __syncthreads();
+  const int outs = a.rows * kLatTileN;
+  for (int i = threadIdx.x; i < outs; i += kThreads) {
+    const int r = i / kLatTileN;
+    const int col = i % kLatTileN;
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += (double)red[(w * kRowsPad + r) * kLatTileN + col];
+    st_dev(&a.lat_part[((size_t)split * a.rows_cap + r) * kLatent + n0 + col], (float)s);
+  }
+  if (publish(&a.counters[tile], slot) != (uint32_t)(kSplitsL - 1)) return false;
+  for (int i = threadIdx.x; i < outs; i += kThreads) {
+    const int r = i / kLatTileN;
+    const int col = i % kLatTileN;
+    float p[kSplitsL];
+#pragma unroll
+    for (int sp = 0; sp < kSplitsL; ++sp)
+      p[sp] = ld_dev(&a.lat_part[((size_t)sp * a.rows_cap + r) * kLatent + n0 + col]);
+    double s = 0.0;
+#pragma unroll
+    for (int sp = 0; sp < kSplitsL; ++sp) s += (double)p[sp];
+    a.latent[(size_t)r * kLatent + n0 + col] = f64_to_bf16_rne(s);
+  }
+  if (threadIdx.x == 0) st_dev(&a.counters[tile], 0u);
+  return true;
+}
+
+// Row group: rows r0..r0+3 (those below `rows`). Every logit is stored; for
+// the fused call each wave w copies row r0 + w into LDS and selects its top-16.
+__device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
+  if (!a.fuse_topk) return;
+  float* lrows = reinterpret_cast<float*>(smem);  // [kRowGroup][kExperts]
+  const int nr = min(kRowGroup, a.rows - r0);
+  for (int i = threadIdx.x; i < nr * kExperts; i += kThreads)
+    lrows[i] = ld_dev(&a.logits[(size_t)r0 * kExperts + i]);
+  __syncthreads();
+  const int w = threadIdx.x >> 6;
+  if (w < nr)
+    topk16_wave(lrows + w * kExperts, a.ids + (size_t)(r0 + w) * kTopK,
+                a.weights + (size_t)(r0 + w) * kTopK);
+  __syncthreads();
+}
+
+// Claim the next group of rows if every router tile has been combined.
+// Returns the group's first row, or -1 when the router phase is not complete
+// or no row is left. `router_done` is thread 0's knowledge that it is complete.
+__device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done, int* slot) {
+  int r = -1;
+  if (threadIdx.x == 0) {
+    if (router_done || ld_dev(&a.counters[kCtrRouter]) == (uint32_t)kRtTiles) {
+      const uint32_t c = add_dev(&a.counters[kCtrRows], (uint32_t)kRowGroup);
+      if (c < (uint32_t)a.rows) r = (int)c;
+    }
+  }
+  return broadcast(r, slot);
+}
+
+// Workgroup b < 448 runs router unit b, the others latent unit b - 448. Row
+// groups (the fused top-16) are taken by the workgroup that combines the last
+// router tile, until none is left, and by every workgroup that combines a
+// latent tile, if the logits are complete by then. These 57 participants each
+// bump kCtrFin once when they stop taking rows; the last resets the row-phase
+// counters for the next call.
+template <int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_route_kernel(DecodeArgs a) {
+  constexpr int kLatBytes = kWaves * rows_kept<NT>() * kLatTileN * 4;
+  constexpr int kRtBytes = kWaves * rows_kept<NT>() * kRtTileE * 8;
+  constexpr int kRowBytes = kRowGroup * kExperts * 4;
+  constexpr int kB0 = kLatBytes > kRtBytes ? kLatBytes : kRtBytes;
+  constexpr int kBytes = kB0 > kRowBytes ? kB0 : kRowBytes;
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
-  __shared__ int flag;
+  __shared__ int slot;
+
   const int b = blockIdx.x;
-  if (b < kLatBlocks)
-    latent_block<NT>(a, b, reinterpret_cast<float*>(smem), &flag);
-  else
-    router_block<NT>(a, b - kLatBlocks, reinterpret_cast<double*>(smem), &flag);
+  bool router_done = false;
+  if (b < kRtUnits) {
+    router_done = router_unit<NT>(a, b, smem, &slot);
+    if (!router_done) return;
+  } else if (!latent_unit<NT>(a, b - kRtUnits, smem, &slot)) {
+    return;
+  }
+  for (int r = claim_rows(a, router_done, &slot); r >= 0; r = claim_rows(a, router_done, &slot))
+    row_group(a, r, smem);
+  if (publish(&a.counters[kCtrFin], &slot) == (uint32_t)(kRowParticipants - 1) && threadIdx.x == 0) {
+    st_dev(&a.counters[kCtrRouter], 0u);
+    st_dev(&a.counters[kCtrRows], 0u);
+    st_dev(&a.counters[kCtrFin], 0u);
+  }
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -314,9 +422,9 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits) {
   size_t off = align256(sizeof(uint32_t) * kDecodeCounters);
   *off_lat = off;
-  off = align256(off + sizeof(float) * kSplits * (size_t)rows_cap * kLatent);
+  off = align256(off + sizeof(float) * kSplitsL * (size_t)rows_cap * kLatent);
   *off_rt = off;
-  off = align256(off + sizeof(double) * kSplits * (size_t)rows_cap * kExperts);
+  off = align256(off + sizeof(double) * kSplitsR * (size_t)rows_cap * kExperts);
   *off_logits = off;
   off = align256(off + sizeof(float) * (size_t)rows_cap * kExperts);
   return off;
@@ -342,9 +450,9 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
   if (rows <= 16)
-    hipLaunchKernelGGL(decode_route_kernel<1>, dim3(kDecodeBlocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_route_kernel<1>, dim3(kGrid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_route_kernel<2>, dim3(kDecodeBlocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_route_kernel<2>, dim3(kGrid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

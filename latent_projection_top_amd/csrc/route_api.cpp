@@ -52,11 +52,9 @@ int run_latent_router(const route_plan* p, const void* x, const void* w_latent, 
   const uint16_t* wb = static_cast<const uint16_t*>(w_latent);
   uint16_t* lb = static_cast<uint16_t*>(latent);
   if (p->mode == ROUTE_MODE_DECODE) {
-    const bool epilogue = fused && rows <= 8;
-    int st = status_of(route::launch_decode_route(xb, wb, w_router, lb, logits, ids, weights,
-                                                  decode_ws(p, ws), rows, p->rows_cap, epilogue, s));
-    if (st != ROUTE_OK || !fused || epilogue) return st;
-    return status_of(route::launch_topk16(logits, ids, weights, rows, s));
+    // decode: one launch; the fused select runs inside the projection kernel
+    return status_of(route::launch_decode_route(xb, wb, w_router, lb, logits, ids, weights,
+                                                decode_ws(p, ws), rows, p->rows_cap, fused, s));
   }
   int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, s));
   if (st != ROUTE_OK) return st;

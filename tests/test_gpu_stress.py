@@ -75,7 +75,7 @@ def test_graph_replay_with_new_banks_and_poisoned_outputs(width):
             log(f"  replay {i}: mismatches so far {mismatches}")
     torch.cuda.synchronize()
     assert mismatches == 0
-    assert int(ws[:512].count_nonzero()) == 0
+    assert int(ws[:256].count_nonzero()) == 0
 
 
 @pytest.mark.timeout(600)
