@@ -28,10 +28,15 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
+# Per-source extra flags. The prefill GEMM keeps its MFMA accumulators in
+# VGPRs (the VGPR form of v_mfma): measured on gfx950, MFMAs accumulating in
+# AGPRs issued at about half the rate when a SIMD held a single wave.
+EXTRA_FLAGS = {"prefill_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

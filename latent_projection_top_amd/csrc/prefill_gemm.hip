@@ -8,243 +8,401 @@
 // M = prefill rows, K = 7168 (the page's per-rank N is 448; one GPU computes
 // all N = 3584 columns).
 //
-// Latent: C[M][3584] = x[M][7168] * W[7168][3584], BF16 MFMA
-// (v_mfma_f32_16x16x32_bf16), FP32 accumulation over all of K in the MFMA
-// accumulators, one nearest-even rounding to BF16 at the end.
+// Latent: C[M][3584] = x[M][7168] * W[7168][3584] on v_mfma_f32_16x16x32_bf16.
+// A running FP32 MFMA accumulator loses accuracy with the length of its chain
+// (each step rounds into a sum that keeps growing), so the accumulators start
+// from zero every 256 K values and are added into a second FP32 sum; the
+// result is rounded to BF16 once, nearest-even.
 //
-// Router: logits[M][896] = x * Wr with Wr in FP32. Each FP32 weight is split
-// exactly into three BF16 parts (w = hi + mid + lo: each step takes the top 8
-// significant bits of what is left; the remainder after two steps has at most
-// 8 significant bits). x is BF16, so every product x*part is exact in FP32 and
-// the contraction runs on the BF16 MFMA at three times the latent's work per
-// weight. Every 32-wide K slice is summed by three MFMAs into a zeroed FP32
-// accumulator and folded into FP64 accumulators; the logits are the FP64 sums
-// rounded once to FP32.
+// Router: logits[M][896] = x * Wr with Wr in FP32. A small pass splits each
+// FP32 weight exactly into three BF16 parts (w = hi + mid + lo: each step
+// takes the top 8 significant bits of what is left; the remainder after two
+// steps has at most 8 significant bits) and stores them as a BF16 matrix
+// [7168][14 expert groups][3 parts][64 experts]. x is BF16, so every product
+// x * part is exact in FP32 and the contraction is a BF16 GEMM with 2688
+// columns. The hi products run in one FP32 chain, the mid and lo products in
+// another (they are 2^-8 smaller and more), both restarted every 256 K values
+// and folded into FP64 sums that are rounded once to FP32.
 //
-// Operand staging: x tiles are K-contiguous and go to LDS as they are. W is
-// stored [K][N] (N contiguous) while the MFMA wants 8 consecutive K values of
-// one column per lane, so each thread transposes the 2 x 8 block it loaded
-// (v_perm on BF16 pairs) and writes K-contiguous columns to LDS. Block tile
-// 128 x 128, 4 waves of 64 x 64, BK = 32, two LDS stages.
+// Tiling for gfx950 (256 CUs): block tile 192 rows x 224 columns (latent) or
+// 192 x 192 (router: 64 experts x 3 parts), so 3072 rows give 256 latent
+// blocks, one per CU. Eight waves, 4 x 2, each 48 rows x (112 | 96) columns
+// with its accumulators in VGPRs: two waves per SIMD keep the matrix core
+// busy where one wave holding everything in AGPRs reaches only about 55% of
+// its rate. K step 64, three LDS stages (156 KB at most). Operands go from global
+// memory straight to LDS (global_load_lds_dwordx4: 64 lanes x 16 bytes land
+// contiguously), so no staging registers are spent on them:
+//   A stage [192 rows][64 k]: 128-byte rows, the 16-byte piece c of row r
+//     stored at position c ^ ((r >> 1) & 7), so the 16 rows one MFMA lane
+//     group reads hit 16 different bank groups;
+//   B stage [cols/32 blocks][64 k][32 cols], W keeps its [K][N] order: the
+//     MFMA wants 8 consecutive K of one column per lane, which
+//     ds_read_tr16_b64 delivers from row-major data (lane L of a 16-lane
+//     group gets element L % 4 of the 8-byte chunks that lanes L / 4 + 4 j
+//     address, j = 0..3). The two 32-byte halves of a 64-byte row are swapped
+//     when (k >> 3) is odd, so the two lane groups of one read phase use
+//     different banks.
 #include "route_device.h"
 #include "route_launch.h"
 
 namespace route {
 
-constexpr int kPBM = 128;
-constexpr int kPBN = 128;
-constexpr int kPBK = 32;
-constexpr int kPThreads = 256;
-constexpr int kPLd = kPBK + 8;  // LDS row stride in BF16 elements (80 bytes)
+constexpr int kGBM = 192;
+constexpr int kGBK = 64;
+constexpr int kGStages = 3;
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGKT = kHidden / kGBK;   // 112 K stages
+constexpr int kGFoldStages = 4;        // accumulators restart every 4 x 64 = 256 K
 constexpr int kPrefillMaxRows = 3072;
+constexpr int kRouterCols = 3 * kExperts;  // 2688: [14 groups][3 parts][64]
 
-static_assert(kHidden % kPBK == 0 && kLatent % kPBN == 0 && kExperts % kPBN == 0, "tiles");
+static_assert(kGKT % kGFoldStages == 0, "fold period");
 
-// Split an FP32 value into three BF16 parts whose sum is exact.
-__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = f32_to_bf16_rne(w);
-  const float r1 = w - __uint_as_float(hi << 16);
-  mid = f32_to_bf16_rne(r1);
-  const float r2 = r1 - __uint_as_float(mid << 16);
-  lo = f32_to_bf16_rne(r2);
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int P>
-struct PrefillSmem {
-  uint16_t a[2][kPBM * kPLd];
-  uint16_t b[2][P][kPBN * kPLd];
+template <bool Router>
+struct GemmShape {
+  static constexpr int BN = Router ? 192 : 224;      // block columns
+  static constexpr int NT = Router ? 6 : 7;          // 16-column MFMA tiles per wave
+  static constexpr int MT = 3;                       // 16-row MFMA tiles per wave
+  static constexpr int NB = BN / 32;                 // 32-column B blocks per stage
+  static constexpr int N = Router ? kRouterCols : kLatent;
+  static constexpr int A_BYTES = kGBM * kGBK * 2;    // 24576
+  static constexpr int B_BYTES = NB * kGBK * 64;     // NB x 4096
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024;     // 1 KB loads per stage (block)
+  static constexpr int B_LOADS = B_BYTES / 1024;
+  static constexpr int LOADS = A_LOADS + B_LOADS;    // dealt round-robin over the waves
+  static constexpr int PER_WAVE = (LOADS + kGWaves - 1) / kGWaves;
+  static_assert(N % BN == 0, "column tiles");
+  static_assert(A_LOADS % kGWaves == 0, "A loads come first and split evenly");
+  static_assert(kGStages * STAGE <= 160 * 1024, "LDS");
 };
 
-// Router == false: W is BF16 [K][N], output BF16. Router == true: W is FP32
-// [K][N], output FP32.
+// Column (within the block tile) of the wave's n-tile j.
 template <bool Router>
-__global__ __launch_bounds__(kPThreads) void prefill_gemm_kernel(const uint16_t* __restrict__ x,
-                                                                 const void* __restrict__ wv,
-                                                                 void* __restrict__ out, int rows,
-                                                                 int n_total) {
-  constexpr int P = Router ? 3 : 1;
-  __shared__ PrefillSmem<P> sm;
+__device__ __forceinline__ constexpr int tile_col(int wn, int j) {
+  return Router ? 64 * (j >> 1) + 32 * wn + 16 * (j & 1) : 112 * wn + 16 * j;
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt low
+  // bits [3:0], high bits [15:14]; expcnt [6:4]; lgkmcnt [11:8])
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Wait until at most `pending` of this wave's global -> LDS loads are in
+// flight; a wave owns PER_WAVE or PER_WAVE - 1 loads of every stage.
+template <int PerWave>
+__device__ __forceinline__ void vm_wait_stages(bool full_wave, int stages_pending) {
+  if (stages_pending == 2) {
+    if (full_wave) vm_wait<2 * PerWave>(); else vm_wait<2 * (PerWave - 1)>();
+  } else if (stages_pending == 1) {
+    if (full_wave) vm_wait<PerWave>(); else vm_wait<PerWave - 1>();
+  } else {
+    vm_wait<0>();
+  }
+}
+
+// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes from
+// base + voff land at LDS address lds + 16 l. Written as inline assembly so
+// that the compiler does not add a wait for every outstanding load before
+// each LDS read (it cannot tell the stages apart); the kernel waits with
+// explicit vmcnt counts instead. M0 carries the LDS address.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "{m0}"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
+
+__device__ __forceinline__ s16x4 lds_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
+}
+
+template <bool Router>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                         void* __restrict__ out, int rows, int mtiles) {
+  using S = GemmShape<Router>;
+  __shared__ __attribute__((aligned(1024))) char smem[kGStages * S::STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int m = lane & 15;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int nbn = n_total / kPBN;
-  const int bn0 = (blockIdx.x % nbn) * kPBN;
-  const int bm0 = (blockIdx.x / nbn) * kPBM;
+  const int wm = wave >> 1;  // 48-row slice
+  const int wn = wave & 1;   // column half
 
-  // A loads: 128 rows x 4 chunks of 8 -> 2 chunks per thread.
-  int a_row[2], a_k[2];
-  bool a_ok[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + i * kPThreads;
-    a_row[i] = c >> 2;
-    a_k[i] = (c & 3) * 8;
-    a_ok[i] = bm0 + a_row[i] < rows;
-  }
-  // B loads: 16 row pairs x 16 column groups of 8 -> one 2 x 8 block per thread.
-  const int b_k = (tid >> 4) * 2;
-  const int b_n = (tid & 15) * 8;
+  // Tile order. The hardware deals blocks round-robin over the 8 XCDs, so
+  // block b is first renumbered (b % 8) * (total / 8) + b / 8 (when that
+  // divides evenly), giving each XCD a contiguous range; the range is then
+  // walked in groups of 8 row tiles, column by column, so that one XCD's L2
+  // holds about 8 A tiles and 4 B tiles at a time.
+  const int ntiles = S::N / S::BN;
+  const int total = mtiles * ntiles;
+  int lin = blockIdx.x;
+  if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int grp = lin / (8 * ntiles);
+  const int first = grp * 8;
+  const int gm = min(mtiles - first, 8);
+  const int loc = lin - grp * 8 * ntiles;
+  const int bm0 = (first + loc % gm) * kGBM;
+  const int bn0 = (loc / gm) * S::BN;
 
-  u32x4 ra[2];
-  u32x4 rb16[2];          // BF16: rows b_k, b_k+1, 8 columns each
-  float rb32[2][8];       // FP32: rows b_k, b_k+1, 8 columns each
-
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * kPBK;
+  // ---- global -> LDS loads: load c of a stage (wave c % 8) -----------------
+  //   c < A_LOADS: A rows 8 c .. 8 c + 7;  else B block (c - A_LOADS) / 4,
+  //   k rows 16 ((c - A_LOADS) % 4) .. + 15.
+  const bool full_wave = wave + kGWaves * (S::PER_WAVE - 1) < S::LOADS;
+  uint32_t off[S::PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      ra[i] = a_ok[i] ? *(const u32x4*)(x + (size_t)(bm0 + a_row[i]) * kHidden + k0 + a_k[i])
-                      : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (!Router) {
-      const uint16_t* w = static_cast<const uint16_t*>(wv);
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        rb16[r] = __builtin_nontemporal_load(
-            (const u32x4*)(w + (size_t)(k0 + b_k + r) * n_total + bn0 + b_n));
+  for (int i = 0; i < S::PER_WAVE; ++i) {
+    const int c = wave + kGWaves * i;
+    if (c < S::A_LOADS) {
+      const int r = 8 * c + (lane >> 3);
+      const int piece = (lane & 7) ^ ((r >> 1) & 7);
+      const int row = min(bm0 + r, rows - 1);
+      off[i] = (uint32_t)(row * kHidden + 8 * piece) * 2u;
     } else {
-      const float* w = static_cast<const float*>(wv);
+      const int ib = min(c, S::LOADS - 1) - S::A_LOADS;
+      const int k = 16 * (ib & 3) + (lane >> 2);
+      const int q = (lane & 3) ^ (((k >> 3) & 1) << 1);
+      off[i] = (uint32_t)(k * S::N + bn0 + 32 * (ib >> 2) + 8 * q) * 2u;
+    }
+  }
+  const char* a_src = reinterpret_cast<const char*>(x);
+  const char* b_src = reinterpret_cast<const char*>(w);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % kGStages) * S::STAGE;
+    const char* ab = a_src + (size_t)kt * (kGBK * 2);
+    const char* bb = b_src + (size_t)kt * ((size_t)kGBK * S::N * 2);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const f32x4 v0 = __builtin_nontemporal_load(
-            (const f32x4*)(w + (size_t)(k0 + b_k + r) * n_total + bn0 + b_n));
-        const f32x4 v1 = __builtin_nontemporal_load(
-            (const f32x4*)(w + (size_t)(k0 + b_k + r) * n_total + bn0 + b_n + 4));
+    for (int i = 0; i < S::PER_WAVE; ++i) {
+      const int c = wave + kGWaves * i;
+      if (i < S::A_LOADS / kGWaves)
+        dma16(ab, off[i], st + c * 1024);
+      else if (c < S::LOADS)
+        dma16(bb, off[i], st + c * 1024);
+    }
+  };
+
+  // ---- LDS -> register operand addresses ----------------------------------
+  // A, tile i, K half s: row 48 wm + 16 i + m, piece 4 s + g (the swizzle
+  // term (row >> 1) & 7 equals (m >> 1) & 7 because 48 wm + 16 i is a
+  // multiple of 16).
+  uint32_t a_rd[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          rb32[r][q] = v0[q];
-          rb32[r][4 + q] = v1[q];
+  for (int s = 0; s < 2; ++s)
+    a_rd[s] = (uint32_t)((48 * wm + m) * 128 + (((4 * s + g) ^ ((m >> 1) & 7)) * 16));
+  // B, 16-column half h of a 32-column block, K rows 8 g + m / 4 (+ 32 s + 4 e),
+  // columns 16 h + 4 (m % 4) .. + 3.
+  uint32_t b_rd[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    b_rd[h] = (uint32_t)(S::A_BYTES + (8 * g + (m >> 2)) * 64 +
+                         ((2 * (h ^ (g & 1)) + ((m & 3) >> 1)) * 16) + (m & 1) * 8);
+
+  struct Ops {
+    bf16x8 a[S::MT];
+    bf16x8 b[S::NT];
+  };
+  auto read_a = [&](uint32_t st, int s, int i) { return lds_b128(st + a_rd[s] + 2048 * i); };
+  auto read_b = [&](uint32_t st, int s, int j) {
+    const int col = tile_col<Router>(wn, j);
+    const uint32_t base = st + b_rd[(col >> 4) & 1] + (col >> 5) * 4096 + 32 * s * 64;
+    const s16x4 lo = lds_tr16(base);
+    const s16x4 hi = lds_tr16(base + 4 * 64);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto stage_lds = [&](int kt) { return lds0 + (kt % kGStages) * S::STAGE; };
+
+  // latent: one chain per tile; router: chains 0, 1 take the hi parts of the
+  // two 16-expert tiles, chains 2, 3 their mid and lo parts
+  f32x4 chain[S::MT][Router ? 4 : S::NT];
+  f32x4 sum32[Router ? 1 : S::MT][Router ? 1 : S::NT];
+  double sum64[Router ? S::MT : 1][Router ? 2 : 1][4];
+#pragma unroll
+  for (int i = 0; i < S::MT; ++i) {
+    if constexpr (Router) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sum64[i][j][t] = 0.0;
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::NT; ++j) sum32[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // One K half (32) of MFMAs, row by row. Each operand register is refilled
+  // with the next K half's value as soon as its last MFMA has been issued
+  // (a[i] after row i, b[j] in the last row), so the next half's operands
+  // arrive while this half's MFMAs run, without a second register set.
+  auto step = [&](Ops& o, bool restart, bool reload, uint32_t st_n, int s_n) {
+#pragma unroll
+    for (int i = 0; i < S::MT; ++i) {
+#pragma unroll
+      for (int j = 0; j < S::NT; ++j) {
+        if constexpr (Router) {
+          const int c = j < 2 ? j : 2 + (j & 1);
+          const bool z = restart && j < 4;  // first MFMA of each chain in the period
+          chain[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[i], o.b[j], z ? zero4 : chain[i][c],
+                                                               0, 0, 0);
+        } else {
+          chain[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[i], o.b[j],
+                                                               restart ? zero4 : chain[i][j], 0, 0, 0);
         }
+        if (reload && i == S::MT - 1) o.b[j] = read_b(st_n, s_n, j);
+        // SB1
       }
+      if (reload) o.a[i] = read_a(st_n, s_n, i);
+      // SB2
     }
   };
 
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *(u32x4*)(&sm.a[buf][a_row[i] * kPLd + a_k[i]]) = ra[i];
-    if constexpr (!Router) {
-      // column c of the 2 x 8 block: (row b_k, row b_k+1) as one BF16 pair
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t v = __builtin_amdgcn_perm(rb16[1][c >> 1], rb16[0][c >> 1], sel);
-        *(uint32_t*)(&sm.b[buf][0][(b_n + c) * kPLd + b_k]) = v;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint32_t h0, m0, l0, h1, m1, l1;
-        split3(rb32[0][c], h0, m0, l0);
-        split3(rb32[1][c], h1, m1, l1);
-        *(uint32_t*)(&sm.b[buf][0][(b_n + c) * kPLd + b_k]) = h0 | (h1 << 16);
-        *(uint32_t*)(&sm.b[buf][1][(b_n + c) * kPLd + b_k]) = m0 | (m1 << 16);
-        *(uint32_t*)(&sm.b[buf][2][(b_n + c) * kPLd + b_k]) = l0 | (l1 << 16);
-      }
-    }
-  };
-
-  f32x4 acc[4][4];
-  double acc64[Router ? 4 : 1][Router ? 4 : 1][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (Router) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc64[i][j][t] = 0.0;
-  }
-
-  constexpr int KT = kHidden / kPBK;
-  load_tile(0);
-  store_tile(0);
+  // Pipeline (three LDS stages, loads two stages ahead). The first K half of
+  // stage kt runs while the second half's operands are read; then every wave
+  // has read all of stage kt, waits for its own loads of stage kt + 1 and
+  // meets the others at the barrier: past it, stage kt + 1 is complete in
+  // LDS and stage kt's buffer takes the loads of stage kt + 3, while the
+  // second half runs and reads the first half of stage kt + 1.
+  issue(0);
+  issue(1);
+  issue(2);
+  vm_wait_stages<S::PER_WAVE>(full_wave, 2);
   __syncthreads();
+  Ops o;
+#pragma unroll
+  for (int i = 0; i < S::MT; ++i) o.a[i] = read_a(stage_lds(0), 0, i);
+#pragma unroll
+  for (int j = 0; j < S::NT; ++j) o.b[j] = read_b(stage_lds(0), 0, j);
+
 #pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
-    bf16x8 af[4];
+  for (int kp = 0; kp < kGKT; kp += kGFoldStages) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *(const bf16x8*)(&sm.a[buf][(wm * 64 + 16 * i + m) * kPLd + 8 * g]);
-    if constexpr (!Router) {
+    for (int u = 0; u < kGFoldStages; ++u) {
+      const int kt = kp + u;
+      step(o, u == 0, true, stage_lds(kt), 1);
+      lgkm_wait0();
+      vm_wait_stages<S::PER_WAVE>(full_wave, kt + 2 < kGKT ? 1 : 0);
+      __syncthreads();
+      if (kt + 3 < kGKT) issue(kt + 3);
+      // (after the last stage this reads a stale buffer; the values go unused)
+      step(o, false, true, stage_lds(kt + 1), 0);
+    }
+    // fold the restarted chains into the long sums
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 bfr = *(const bf16x8*)(&sm.b[buf][0][(wn * 64 + 16 * j + m) * kPLd + 8 * g]);
+    for (int i = 0; i < S::MT; ++i) {
+      if constexpr (Router) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
-      }
-    } else {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int off = (wn * 64 + 16 * j + m) * kPLd + 8 * g;
-        const bf16x8 bl = *(const bf16x8*)(&sm.b[buf][2][off]);
-        const bf16x8 bmid = *(const bf16x8*)(&sm.b[buf][1][off]);
-        const bf16x8 bh = *(const bf16x8*)(&sm.b[buf][0][off]);
+          for (int t = 0; t < 4; ++t)
+            sum64[i][j][t] += (double)chain[i][j][t] + (double)chain[i][j + 2][t];
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
-          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bl, t4, 0, 0, 0);
-          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bmid, t4, 0, 0, 0);
-          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bh, t4, 0, 0, 0);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc64[i][j][t] += (double)t4[t];
-        }
+        for (int j = 0; j < S::NT; ++j) sum32[i][j] += chain[i][j];
       }
     }
-    if (kt + 1 < KT) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
   // lane (g, m) of tile (i, j) holds row 16 i + 4 g + t, column 16 j + m
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < S::MT; ++i) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = bm0 + wm * 64 + 16 * i + 4 * g + t;
+      const int row = bm0 + 48 * wm + 16 * i + 4 * g + t;
       if (row >= rows) continue;
+      if constexpr (Router) {
+        // expert group bn0 / 192, experts 32 wn + 16 j + m of its 64
+        const int e0 = (bn0 / 192) * 64 + 32 * wn + m;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = bn0 + wn * 64 + 16 * j + m;
-        if constexpr (!Router)
-          static_cast<uint16_t*>(out)[(size_t)row * n_total + col] = f32_to_bf16_rne(acc[i][j][t]);
-        else
-          static_cast<float*>(out)[(size_t)row * n_total + col] = (float)acc64[i][j][t];
+        for (int j = 0; j < 2; ++j)
+          static_cast<float*>(out)[(size_t)row * kExperts + e0 + 16 * j] = (float)sum64[i][j][t];
+      } else {
+#pragma unroll
+        for (int j = 0; j < S::NT; ++j) {
+          const int col = bn0 + tile_col<false>(wn, j) + m;
+          static_cast<uint16_t*>(out)[(size_t)row * kLatent + col] = f32_to_bf16_rne(sum32[i][j][t]);
+        }
       }
     }
   }
 }
 
+// Split the FP32 router weight into its three exact BF16 parts, stored as
+// parts[k][e / 64][p][e % 64]. One thread per 8 consecutive experts of a row.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
+                                                           uint16_t* __restrict__ parts) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int k = t / (kExperts / 8);
+  const int e = (t % (kExperts / 8)) * 8;
+  if (k >= kHidden) return;
+  const f32x4 v0 = __builtin_nontemporal_load((const f32x4*)(wr + (size_t)k * kExperts + e));
+  const f32x4 v1 = __builtin_nontemporal_load((const f32x4*)(wr + (size_t)k * kExperts + e + 4));
+  uint32_t p[3][4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float wv = c < 4 ? v0[c] : v1[c - 4];
+    const uint32_t hi = f32_to_bf16_rne(wv);
+    const float r1 = wv - __uint_as_float(hi << 16);
+    const uint32_t mid = f32_to_bf16_rne(r1);
+    const float r2 = r1 - __uint_as_float(mid << 16);
+    const uint32_t lo = f32_to_bf16_rne(r2);
+    const int sh = (c & 1) * 16;
+    if ((c & 1) == 0) p[0][c >> 1] = p[1][c >> 1] = p[2][c >> 1] = 0u;
+    p[0][c >> 1] |= hi << sh;
+    p[1][c >> 1] |= mid << sh;
+    p[2][c >> 1] |= lo << sh;
+  }
+  uint16_t* dst = parts + (size_t)k * kRouterCols + (e / 64) * 192 + (e % 64);
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+    *(u32x4*)(dst + 64 * q) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
+}
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits) {
-  *off_logits = 0;
-  return align256(sizeof(float) * (size_t)rows_cap * kExperts);
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts) {
+  *off_parts = 0;
+  const size_t parts = align256(sizeof(uint16_t) * (size_t)kHidden * kRouterCols);
+  *off_logits = parts;
+  return parts + align256(sizeof(float) * (size_t)rows_cap * kExperts);
 }
 
 hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
                                  int rows, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
-  const int mb = (rows + kPBM - 1) / kPBM;
-  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(mb * (kLatent / kPBN)), dim3(kPThreads), 0,
-                     stream, x, (const void*)w_latent, (void*)latent, rows, kLatent);
+  const int mt = (rows + kGBM - 1) / kGBM;
+  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(mt * (kLatent / 224)), dim3(kGThreads), 0,
+                     stream, x, w_latent, (void*)latent, rows, mt);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, float* logits, int rows,
-                                 hipStream_t stream) {
+hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
+                                 float* logits, int rows, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
-  const int mb = (rows + kPBM - 1) / kPBM;
-  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(mb * (kExperts / kPBN)), dim3(kPThreads), 0,
-                     stream, x, (const void*)w_router, (void*)logits, rows, kExperts);
+  hipLaunchKernelGGL(router_split_kernel, dim3(kHidden * (kExperts / 8) / 256), dim3(256), 0, stream,
+                     w_router, parts);
+  const int mt = (rows + kGBM - 1) / kGBM;
+  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), 0,
+                     stream, x, (const uint16_t*)parts, (void*)logits, rows, mt);
   return hipGetLastError();
 }
 

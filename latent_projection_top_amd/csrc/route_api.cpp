@@ -18,6 +18,7 @@ struct route_plan {
   size_t off_lat;     // decode: latent partials
   size_t off_rt;      // decode: router partials
   size_t off_logits;  // logits buffer for route_fused with logits == NULL
+  size_t off_parts;   // prefill: BF16 parts of the router weight
 };
 
 namespace {
@@ -58,7 +59,8 @@ int run_latent_router(const route_plan* p, const void* x, const void* w_latent, 
   }
   int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, s));
   if (st != ROUTE_OK) return st;
-  st = status_of(route::launch_prefill_router(xb, w_router, logits, rows, s));
+  uint16_t* parts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p->off_parts);
+  st = status_of(route::launch_prefill_router(xb, w_router, parts, logits, rows, s));
   if (st != ROUTE_OK || !fused) return st;
   return status_of(route::launch_topk16(logits, ids, weights, rows, s));
 }
@@ -92,9 +94,10 @@ int route_prepare(const route_config* cfg, route_plan** out) {
   p->device = cfg->device;
   if (p->mode == ROUTE_MODE_DECODE) {
     p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, &p->off_lat, &p->off_rt, &p->off_logits);
+    p->off_parts = 0;
   } else {
     p->off_lat = p->off_rt = 0;
-    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits);
+    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits, &p->off_parts);
   }
   *out = p;
   return ROUTE_OK;

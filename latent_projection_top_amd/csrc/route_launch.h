@@ -15,7 +15,7 @@ struct DecodeWorkspace {
 };
 
 size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits);
-size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits);
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts);
 
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
@@ -28,7 +28,8 @@ hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int 
 hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
                                  int rows, hipStream_t stream);
 
-hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, float* logits, int rows,
-                                 hipStream_t stream);
+// parts: workspace for the three BF16 parts of w_router ([7168][2688] BF16)
+hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
+                                 float* logits, int rows, hipStream_t stream);
 
 }  // namespace route
