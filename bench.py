@@ -14,6 +14,18 @@ the 3072-row prefill chunk, the decode kernel's HBM roofline fraction, the
 prefill MFMA fraction, and the CPU oracle timed on this host (a reported
 baseline only).
 
+Roofline: a decode route is one kernel launch, so the kernel's average launch
+duration is the event-timed graph replay divided by the launches in it (it
+includes the ~1 us between back-to-back launches; event pairs around single
+launches would add far more). The algorithmic bytes of one launch (both
+weights once + the rows' inputs and outputs) divided by that duration is
+`achieved`. `traffic` is the HBM bytes
+per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+valid only while the kernel source is unchanged.
+
+--profile-pass runs only what the counter runs need: 64 headline decode
+launches and a plain 512 MiB device copy (the counters' calibration).
+
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
@@ -126,6 +138,20 @@ def time_graph(g, replays: int, torch):
     return start.elapsed_time(end) / replays
 
 
+def profile_pass(rows: int, copies, banks, route, torch):
+    """Short run for the rocprofv3 counter passes: headline decode launches and
+    one plain copy of known size."""
+    d = DecodeSetup(rows, copies, banks, route, torch)
+    for _ in range(8):
+        d.run_all()
+    torch.cuda.synchronize()
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"profile pass: {8 * len(copies)} decode launches of {rows} rows, one 512 MiB copy")
+
+
 def cpu_baseline(rows: int, budget_s: float):
     """The oracle, as it is, on this host: route_ref_widened on 8-row batches
     with the weights widened to float64 once outside the timed region."""
@@ -165,6 +191,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline width only")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="only the launches the rocprofv3 counter passes need")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -193,6 +221,9 @@ def main():
     for c in range(copies_n):
         copies.append((bf16(gen.latent_weight(c)), torch.from_numpy(gen.router_weight(c)).cuda()))
     banks = [bf16(gen.hidden(20, bank=4000 + b)) for b in range(copies_n)]
+    if args.profile_pass:
+        profile_pass(args.rows, copies, banks, route, torch)
+        return
 
     results = {}
     widths = [args.rows] + ([int(w) for w in args.widths.split(",") if int(w) != args.rows]
@@ -211,15 +242,17 @@ def main():
         results[rows] = us
         log(f"decode rows={rows}: {us:.2f} us per route ({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
         if rows == args.rows:
-            head = (us, ms_rep / copies_n)
+            head = (us, ms_rep / copies_n, ms_rep / copies_n)
         del g, d
 
-    us8, ms_step = head
-    achieved = decode_bytes(args.rows) / (us8 * 1e-6) / 1e9
+    us8, ms_step, kernel_ms = head
+    achieved = decode_bytes(args.rows) / (kernel_ms * 1e-3) / 1e9
     traffic = committed_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": "decode_route_kernel<1>",
+                "traffic": traffic,
+                "kernel": "decode_route_kernel<1>" if args.rows <= 16 else "decode_route_kernel<2>",
+                "kernel_us_per_launch": round(kernel_ms * 1000.0, 3),
                 "algorithmic_bytes_per_launch": decode_bytes(args.rows)}
 
     prefill = None
@@ -255,7 +288,8 @@ def main():
             "latent_router_us": round(t_lr, 2), "topk16_us": round(t_tk, 2),
             "mfma_tflops": round(gemm_flops / (t_lr * 1e-6) / 1e12, 1),
             "mfma_frac": round(gemm_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-            "router_variant": "bf16x3 split on BF16 MFMA, FP32 runs of 32 folded into FP64",
+            "router_variant": "FP32 weight split into 3 exact BF16 parts, BF16 MFMA, FP32 chains "
+                              "restarted every 256 K and folded into FP64",
         }
         log(f"prefill 3072: {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
             f"{t_lr:.1f} us = {prefill['mfma_tflops']} TFLOP/s, top-16 {t_tk:.1f} us")
