@@ -354,18 +354,16 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
 }
 
 // Row group: rows r0..r0+3 (those below `rows`). Every logit is stored; for
-// the fused call each wave w copies row r0 + w into LDS and selects its top-16.
+// the fused call wave w selects the top-16 of row r0 + w, reading the logits
+// with coherent loads (other workgroups of this launch wrote them).
 __device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
   if (!a.fuse_topk) return;
-  float* lrows = reinterpret_cast<float*>(smem);  // [kRowGroup][kExperts]
+  uint64_t* scratch = reinterpret_cast<uint64_t*>(smem);
   const int nr = min(kRowGroup, a.rows - r0);
-  for (int i = threadIdx.x; i < nr * kExperts; i += kThreads)
-    lrows[i] = ld_dev(&a.logits[(size_t)r0 * kExperts + i]);
-  __syncthreads();
   const int w = threadIdx.x >> 6;
   if (w < nr)
-    topk16_wave(lrows + w * kExperts, a.ids + (size_t)(r0 + w) * kTopK,
-                a.weights + (size_t)(r0 + w) * kTopK);
+    topk16_wave<true>(a.logits + (size_t)(r0 + w) * kExperts, a.ids + (size_t)(r0 + w) * kTopK,
+                      a.weights + (size_t)(r0 + w) * kTopK, scratch + w * kTopkScratch);
   __syncthreads();
 }
 
@@ -394,7 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_route_kernel(DecodeArgs a) {
   constexpr int kLatBytes = kWaves * rows_kept<NT>() * kLatTileN * 4;
   constexpr int kRtBytes = kWaves * rows_kept<NT>() * kRtTileE * 8;
-  constexpr int kRowBytes = kRowGroup * kExperts * 4;
+  constexpr int kRowBytes = kRowGroup * kTopkScratch * 8;
   constexpr int kB0 = kLatBytes > kRtBytes ? kLatBytes : kRtBytes;
   constexpr int kBytes = kB0 > kRowBytes ? kB0 : kRowBytes;
   __shared__ __attribute__((aligned(16))) char smem[kBytes];

@@ -85,6 +85,13 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inverse of logit_key up to the sign of zero and the NaN payload, neither of
+// which changes the sigmoid: key 0 is NaN.
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
   uint64_t hi = a > b ? a : b;
   uint64_t lo = a > b ? b : a;
@@ -92,13 +99,6 @@ __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
   b = lo;
 }
 
-// One wave selects the 16 largest of a row's 896 logits and writes ids and
-// normalised sigmoid weights. Lane l owns experts l, l+64, ..., l+832 and keeps
-// them as 64-bit keys (logit key << 32 | ~index), sorted descending with a
-// Batcher odd-even merge network. Sixteen rounds then take the wave-wide
-// largest head: a DPP max over the 32-bit logit keys, a ballot for the lanes
-// that hold it, and (only on an exact logit tie) a second max over the index
-// half to pick the lowest expert index. The winner pops its head.
 // Coherent selects the load used for the logits: a device-scope atomic load
 // when other workgroups of the same kernel wrote them (the fused epilogue).
 template <bool Coherent = false>
@@ -109,19 +109,39 @@ __device__ __forceinline__ float load_logit(const float* p) {
     return *p;
 }
 
-template <bool Coherent = false>
-__device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32_t* __restrict__ ids,
-                                            float* __restrict__ weights) {
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// 64-bit selection key of expert idx: logit key << 32 | ~idx. Keys are
+// distinct and their order is (logit descending, index ascending).
+template <bool Coherent>
+__device__ __forceinline__ uint64_t select_key(const float* row, uint32_t idx) {
+  return ((uint64_t)logit_key(load_logit<Coherent>(row + idx)) << 32) | (uint64_t)(~idx);
+}
+
+// Fallback selection (many keys at or above the threshold, e.g. large exact
+// ties): lane-local Batcher odd-even merge sort of the 14 keys, then sixteen
+// rounds that take the wave-wide largest head (DPP max over the 32-bit logit
+// key, a ballot for the lanes that hold it, a second max over the index half
+// on an exact tie) and pop it. Lane s < 16 gets the s-th expert and its
+// logit key.
+__device__ __forceinline__ void topk16_rounds(const uint64_t (&keys)[14], uint32_t& my_idx,
+                                              uint32_t& my_key) {
   const int lane = threadIdx.x & (kWave - 1);
   uint64_t c[16];
 #pragma unroll
-  for (int i = 0; i < 14; ++i) {
-    const uint32_t idx = (uint32_t)(i * kWave + lane);
-    c[i] = ((uint64_t)logit_key(load_logit<Coherent>(row + idx)) << 32) | (uint64_t)(~idx);
-  }
+  for (int i = 0; i < 14; ++i) c[i] = keys[i];
   c[14] = 0;
   c[15] = 0;
-  // Batcher odd-even merge sort, 16 inputs, descending.
 #pragma unroll
   for (int p = 1; p < 16; p <<= 1) {
 #pragma unroll
@@ -135,7 +155,8 @@ __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32
       }
     }
   }
-  uint32_t my_idx = 0;
+  my_idx = 0;
+  my_key = 0;
 #pragma unroll 1
   for (int slot = 0; slot < kTopK; ++slot) {
     const uint32_t hk = (uint32_t)(c[0] >> 32);
@@ -149,17 +170,84 @@ __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32
       lo_best = wave_max_u32(hk == m ? (uint32_t)c[0] : 0u);
     }
     const bool win = (hk == m) && ((uint32_t)c[0] == lo_best);
-    if (lane == slot) my_idx = min(~lo_best, (uint32_t)(kExperts - 1));  // always a real entry
+    if (lane == slot) {
+      my_idx = min(~lo_best, (uint32_t)(kExperts - 1));  // always a real entry
+      my_key = m;
+    }
     if (win) {
 #pragma unroll
       for (int i = 0; i < 13; ++i) c[i] = c[i + 1];
       c[13] = 0;
     }
   }
-  // Weights: sigmoid in FP64, normalised over the 16 selected (fixed tree).
+}
+
+// LDS (uint64 slots) one wave of topk16_wave needs.
+constexpr int kTopkScratch = 64 + 64 + kTopK;
+
+// One wave selects the 16 largest of a row's 896 logits and writes ids (in
+// selection order) and normalised sigmoid weights. Lane l owns experts l,
+// l + 64, ..., l + 832 as distinct 64-bit keys.
+//   1. Threshold: t0 = the 16th largest of the 64 lane maxima (each lane
+//      ranks its maximum against all 64 through LDS). At least 16 keys are
+//      >= t0, so the top 16 are among them.
+//   2. The keys >= t0 (typically a few dozen) are compacted into LDS in
+//      ballot order; each ranks itself against all of them, and rank r < 16
+//      is the r-th selected expert.
+//   3. More than 64 keys >= t0 (only with large exact ties) take the
+//      sort-and-rounds fallback, which selects the same experts.
+// scratch: kTopkScratch uint64 slots of LDS owned by this wave. Waves are
+// independent (no workgroup barrier inside).
+template <bool Coherent = false>
+__device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32_t* __restrict__ ids,
+                                            float* __restrict__ weights, uint64_t* scratch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t c[14];
+#pragma unroll
+  for (int i = 0; i < 14; ++i) c[i] = select_key<Coherent>(row, (uint32_t)(i * kWave + lane));
+  uint64_t mx = c[0];
+#pragma unroll
+  for (int i = 1; i < 14; ++i) mx = c[i] > mx ? c[i] : mx;
+
+  uint64_t* lmax = scratch;
+  uint64_t* cand = scratch + 64;
+  uint64_t* sel = scratch + 128;
+  // (one wave's LDS accesses are performed in order: a read after a write
+  // sees it without a barrier)
+  lmax[lane] = mx;
+  uint32_t rk = 0;
+#pragma unroll 8
+  for (int j = 0; j < kWave; ++j) rk += lmax[j] > mx ? 1u : 0u;
+  // the 64 maxima are distinct, so exactly one lane has rank 15
+  const uint64_t t0 = readlane_u64(mx, __builtin_ctzll(ballot(rk == 15u)));
+
+  uint32_t n = 0;  // keys >= t0 so far (wave-uniform)
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    const bool p = c[i] >= t0;
+    const uint64_t msk = ballot(p);
+    const uint32_t pos = n + lanes_below(msk);
+    if (p && pos < (uint32_t)kWave) cand[pos] = c[i];
+    n += (uint32_t)__builtin_popcountll(msk);
+  }
+  uint32_t my_idx, my_key;
+  if (n <= (uint32_t)kWave) {
+    const uint64_t mine = (uint32_t)lane < n ? cand[lane] : 0ull;
+    uint32_t r = 0;
+    for (uint32_t j = 0; j < n; ++j) r += cand[j] > mine ? 1u : 0u;
+    if ((uint32_t)lane < n && r < (uint32_t)kTopK) sel[r] = mine;
+    const uint64_t k = lane < kTopK ? sel[lane] : 0ull;
+    my_idx = min(~(uint32_t)k, (uint32_t)(kExperts - 1));
+    my_key = (uint32_t)(k >> 32);
+  } else {
+    topk16_rounds(c, my_idx, my_key);
+  }
+
+  // Weights: sigmoid in FP64 of the selected logit (recovered from its key),
+  // normalised over the 16 selected (fixed tree).
   double s = 0.0;
   if (lane < kTopK) {
-    const double v = (double)load_logit<Coherent>(row + my_idx);
+    const double v = (double)key_logit(my_key);
     s = 1.0 / (1.0 + exp(-v));
   }
   double tot = s;

@@ -14,10 +14,11 @@ constexpr int kTopkRowsPerBlock = 4;
 __global__ __launch_bounds__(kWave * kTopkRowsPerBlock) void topk16_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
     int rows) {
+  __shared__ uint64_t scratch[kTopkRowsPerBlock][kTopkScratch];
   const int row = blockIdx.x * kTopkRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole waves leave together
   topk16_wave(logits + (size_t)row * kExperts, ids + (size_t)row * kTopK,
-              weights + (size_t)row * kTopK);
+              weights + (size_t)row * kTopK, scratch[threadIdx.x >> 6]);
 }
 
 hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,

@@ -71,6 +71,31 @@ def test_topk16_dense_ties_and_specials():
     assert compare.weights_check(w[fin], rw[fin])["fail"] == 0
 
 
+def clustered_rows(n, seed):
+    """Rows whose largest logits sit in 16 of the 64 lanes (expert index mod
+    64): one lane all 10.0, fifteen lanes uniform in [10.5, 11]. The 16th
+    largest lane maximum is then 10.0 and about 210 keys lie above it, more
+    than the 64 the threshold path compacts, so these rows take the
+    sort-and-rounds path."""
+    r = np.random.default_rng(seed)
+    L = r.standard_normal((n, 896)).astype(np.float32)
+    e = np.arange(896)
+    for i in range(n):
+        lanes = r.permutation(64)[:16]
+        for j, l in enumerate(lanes):
+            m = (e % 64) == l
+            L[i, m] = 10.0 if j == 0 else (10.5 + 0.5 * r.random(m.sum())).astype(np.float32)
+    return L
+
+
+def test_topk16_clustered_lanes():
+    log("topk16 clustered lanes (more than 64 keys above the threshold)")
+    plan = route.Plan(route.MODE_PREFILL, 256)
+    L = np.concatenate([clustered_rows(128, 11), np.random.default_rng(12).standard_normal((128, 896))
+                        .astype(np.float32)])
+    check(L, *run_topk(plan, L))
+
+
 def test_topk16_near_tie_sample():
     log("topk16 near-tie sample 20000 rows")
     plan = route.Plan(route.MODE_PREFILL, 3072)
