@@ -18,6 +18,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------ conversions --
 
@@ -182,20 +183,22 @@ __device__ __forceinline__ void topk16_rounds(const uint64_t (&keys)[14], uint32
   }
 }
 
-// LDS (uint64 slots) one wave of topk16_wave needs.
-constexpr int kTopkScratch = 64 + 64 + kTopK;
+// LDS (uint64 slots) one wave of topk16_wave needs: 64 lane maxima, 64
+// candidates + 8 zero pads, 16 selected.
+constexpr int kTopkScratch = 64 + 72 + kTopK;
 
 // One wave selects the 16 largest of a row's 896 logits and writes ids (in
 // selection order) and normalised sigmoid weights. Lane l owns experts l,
 // l + 64, ..., l + 832 as distinct 64-bit keys.
-//   1. Threshold: t0 = the 16th largest of the 64 lane maxima (each lane
-//      ranks its maximum against all 64 through LDS). At least 16 keys are
+//   1. Threshold: t0 = the 16th largest of the 64 lane maxima; every lane
+//      ranks its maximum against all 64 through LDS. At least 16 keys are
 //      >= t0, so the top 16 are among them.
-//   2. The keys >= t0 (typically a few dozen) are compacted into LDS in
-//      ballot order; each ranks itself against all of them, and rank r < 16
-//      is the r-th selected expert.
-//   3. More than 64 keys >= t0 (only with large exact ties) take the
-//      sort-and-rounds fallback, which selects the same experts.
+//   2. The keys >= t0 (typically about 20) are compacted into LDS in ballot
+//      order; each ranks itself against all of them (keys are distinct), and
+//      rank r < 16 is the r-th selected expert.
+//   3. More than 64 keys >= t0 (the largest logits crowded into a few
+//      lanes) take the sort-and-rounds fallback, which selects the same
+//      experts.
 // scratch: kTopkScratch uint64 slots of LDS owned by this wave. Waves are
 // independent (no workgroup barrier inside).
 template <bool Coherent = false>
@@ -211,13 +214,16 @@ __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32
 
   uint64_t* lmax = scratch;
   uint64_t* cand = scratch + 64;
-  uint64_t* sel = scratch + 128;
+  uint64_t* sel = scratch + 64 + 72;
   // (one wave's LDS accesses are performed in order: a read after a write
   // sees it without a barrier)
   lmax[lane] = mx;
   uint32_t rk = 0;
-#pragma unroll 8
-  for (int j = 0; j < kWave; ++j) rk += lmax[j] > mx ? 1u : 0u;
+#pragma unroll
+  for (int j = 0; j < kWave; j += 2) {
+    const u64x2 v = *reinterpret_cast<const u64x2*>(lmax + j);
+    rk += (v[0] > mx ? 1u : 0u) + (v[1] > mx ? 1u : 0u);
+  }
   // the 64 maxima are distinct, so exactly one lane has rank 15
   const uint64_t t0 = readlane_u64(mx, __builtin_ctzll(ballot(rk == 15u)));
 
@@ -232,9 +238,14 @@ __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32
   }
   uint32_t my_idx, my_key;
   if (n <= (uint32_t)kWave) {
+    // zero pads up to a multiple of 8: a zero key is below every real key
+    if (lane < 8) cand[n + lane] = 0ull;
     const uint64_t mine = (uint32_t)lane < n ? cand[lane] : 0ull;
     uint32_t r = 0;
-    for (uint32_t j = 0; j < n; ++j) r += cand[j] > mine ? 1u : 0u;
+    for (uint32_t j = 0; j < n; j += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r += cand[j + q] > mine ? 1u : 0u;
+    }
     if ((uint32_t)lane < n && r < (uint32_t)kTopK) sel[r] = mine;
     const uint64_t k = lane < kTopK ? sel[lane] : 0ull;
     my_idx = min(~(uint32_t)k, (uint32_t)(kExperts - 1));
