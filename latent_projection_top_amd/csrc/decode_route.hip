@@ -368,13 +368,15 @@ __device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
 }
 
 // Claim the next group of rows if every router tile has been combined.
+// Group 0 (rows 0..3) belongs to the workgroup that completed the router,
+// which starts on it without a claim; the counter hands out the later groups.
 // Returns the group's first row, or -1 when the router phase is not complete
 // or no row is left. `router_done` is thread 0's knowledge that it is complete.
 __device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done, int* slot) {
   int r = -1;
   if (threadIdx.x == 0) {
     if (router_done || ld_dev(&a.counters[kCtrRouter]) == (uint32_t)kRtTiles) {
-      const uint32_t c = add_dev(&a.counters[kCtrRows], (uint32_t)kRowGroup);
+      const uint32_t c = kRowGroup + add_dev(&a.counters[kCtrRows], (uint32_t)kRowGroup);
       if (c < (uint32_t)a.rows) r = (int)c;
     }
   }
@@ -406,6 +408,7 @@ void decode_route_kernel(DecodeArgs a) {
   } else if (!latent_unit<NT>(a, b - kRtUnits, smem, &slot)) {
     return;
   }
+  if (router_done) row_group(a, 0, smem);
   for (int r = claim_rows(a, router_done, &slot); r >= 0; r = claim_rows(a, router_done, &slot))
     row_group(a, r, smem);
   if (publish(&a.counters[kCtrFin], &slot) == (uint32_t)(kRowParticipants - 1) && threadIdx.x == 0) {
