@@ -119,6 +119,19 @@ int route_fused(const route_plan* plan, const void* x, const void* w_latent,
                 const float* w_router, void* latent, float* logits, int32_t* ids,
                 float* weights, void* workspace, int32_t rows, void* stream);
 
+/* Sharded top-16: the selection half of a route whose 896 experts are split
+ * into `shards` contiguous shards of 896 / shards experts (shards in {1, 2, 4,
+ * 7, 8, 14, 16, 28, 32, 56}: a divisor of 896 with at least 16 experts per
+ * shard; 8 and 16 are the tensor-parallel widths of page "Use two row blocks
+ * for eight-row Kimi paired gathers", whose per-rank router output is 56
+ * experts). Stage 1 selects each shard's local top-16 into the workspace,
+ * stage 2 merges the 16 * shards candidates into the global top-16 and its
+ * weights. The merge is exact: the output is bitwise that of route_topk16 on
+ * the same logits. Any other `shards` is ROUTE_E_ARG; `workspace` is the
+ * plan's workspace (its candidate area is used; no counters). */
+int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t shards, int32_t* ids,
+                         float* weights, void* workspace, int32_t rows, void* stream);
+
 /* Free a plan (NULL is accepted). */
 void route_destroy(route_plan* plan);
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libroute.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route_api.cpp", "topk16.hip", "decode_route.hip", "prefill_gemm.hip"]
+SOURCES = ["route_api.cpp", "topk16.hip", "topk16_sharded.hip", "decode_route.hip", "prefill_gemm.hip"]
 HEADERS = ["route_device.h", "route_launch.h"]
 
 COMMON_FLAGS = [

@@ -420,7 +420,8 @@ void decode_route_kernel(DecodeArgs a) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits) {
+size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits,
+                              size_t* off_cand) {
   size_t off = align256(sizeof(uint32_t) * kDecodeCounters);
   *off_lat = off;
   off = align256(off + sizeof(float) * kSplitsL * (size_t)rows_cap * kLatent);
@@ -428,6 +429,8 @@ size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, siz
   off = align256(off + sizeof(double) * kSplitsR * (size_t)rows_cap * kExperts);
   *off_logits = off;
   off = align256(off + sizeof(float) * (size_t)rows_cap * kExperts);
+  *off_cand = off;
+  off = align256(off + sizeof(uint64_t) * (size_t)rows_cap * kTopkMaxShards * kTopK);
   return off;
 }
 

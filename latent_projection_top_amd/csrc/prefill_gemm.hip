@@ -379,11 +379,13 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts) {
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand) {
   *off_parts = 0;
-  const size_t parts = align256(sizeof(uint16_t) * (size_t)kHidden * kRouterCols);
-  *off_logits = parts;
-  return parts + align256(sizeof(float) * (size_t)rows_cap * kExperts);
+  size_t off = align256(sizeof(uint16_t) * (size_t)kHidden * kRouterCols);
+  *off_logits = off;
+  off += align256(sizeof(float) * (size_t)rows_cap * kExperts);
+  *off_cand = off;
+  return off + align256(sizeof(uint64_t) * (size_t)rows_cap * kTopkMaxShards * kTopK);
 }
 
 hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,

@@ -19,6 +19,7 @@ struct route_plan {
   size_t off_rt;      // decode: router partials
   size_t off_logits;  // logits buffer for route_fused with logits == NULL
   size_t off_parts;   // prefill: BF16 parts of the router weight
+  size_t off_cand;    // sharded top-16 candidates
 };
 
 namespace {
@@ -93,11 +94,12 @@ int route_prepare(const route_config* cfg, route_plan** out) {
   p->rows_cap = cfg->rows;
   p->device = cfg->device;
   if (p->mode == ROUTE_MODE_DECODE) {
-    p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, &p->off_lat, &p->off_rt, &p->off_logits);
+    p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, &p->off_lat, &p->off_rt, &p->off_logits,
+                                                &p->off_cand);
     p->off_parts = 0;
   } else {
     p->off_lat = p->off_rt = 0;
-    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits, &p->off_parts);
+    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits, &p->off_parts, &p->off_cand);
   }
   *out = p;
   return ROUTE_OK;
@@ -141,6 +143,19 @@ int route_fused(const route_plan* plan, const void* x, const void* w_latent, con
                      : reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_logits);
   return run_latent_router(plan, x, w_latent, w_router, latent, lg, ids, weights, workspace, rows,
                            true, static_cast<hipStream_t>(stream));
+}
+
+int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t shards, int32_t* ids,
+                         float* weights, void* workspace, int32_t rows, void* stream) {
+  if (!plan || !logits || !ids || !weights || !workspace) return ROUTE_E_ARG;
+  if (!route::topk16_shards_valid(shards)) return ROUTE_E_ARG;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(logits) || misaligned(ids) || misaligned(weights) || misaligned(workspace))
+    return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + plan->off_cand);
+  return status_of(route::launch_topk16_sharded(logits, shards, ids, weights, cand, rows,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 void route_destroy(route_plan* plan) { delete plan; }

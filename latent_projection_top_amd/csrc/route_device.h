@@ -129,20 +129,19 @@ __device__ __forceinline__ uint64_t select_key(const float* row, uint32_t idx) {
   return ((uint64_t)logit_key(load_logit<Coherent>(row + idx)) << 32) | (uint64_t)(~idx);
 }
 
-// Fallback selection (many keys at or above the threshold, e.g. large exact
-// ties): lane-local Batcher odd-even merge sort of the 14 keys, then sixteen
-// rounds that take the wave-wide largest head (DPP max over the 32-bit logit
-// key, a ballot for the lanes that hold it, a second max over the index half
-// on an exact tie) and pop it. Lane s < 16 gets the s-th expert and its
-// logit key.
-__device__ __forceinline__ void topk16_rounds(const uint64_t (&keys)[14], uint32_t& my_idx,
-                                              uint32_t& my_key) {
+// Fallback selection (many keys at or above the threshold: the largest logits
+// crowded into a few lanes, or large exact ties): lane-local Batcher
+// odd-even merge sort of the keys (padded to 16), then sixteen rounds that
+// take the wave-wide largest head (DPP max over the 32-bit logit key, a
+// ballot for the lanes that hold it, a second max over the index half on an
+// exact tie) and pop it. Lane s < 16 gets the s-th key.
+template <int P>
+__device__ __forceinline__ uint64_t select16_rounds(const uint64_t (&keys)[P]) {
+  static_assert(P >= 1 && P <= 14, "keys per lane");
   const int lane = threadIdx.x & (kWave - 1);
   uint64_t c[16];
 #pragma unroll
-  for (int i = 0; i < 14; ++i) c[i] = keys[i];
-  c[14] = 0;
-  c[15] = 0;
+  for (int i = 0; i < 16; ++i) c[i] = i < P ? keys[i] : 0ull;
 #pragma unroll
   for (int p = 1; p < 16; p <<= 1) {
 #pragma unroll
@@ -156,8 +155,7 @@ __device__ __forceinline__ void topk16_rounds(const uint64_t (&keys)[14], uint32
       }
     }
   }
-  my_idx = 0;
-  my_key = 0;
+  uint64_t mine = 0;
 #pragma unroll 1
   for (int slot = 0; slot < kTopK; ++slot) {
     const uint32_t hk = (uint32_t)(c[0] >> 32);
@@ -171,46 +169,39 @@ __device__ __forceinline__ void topk16_rounds(const uint64_t (&keys)[14], uint32
       lo_best = wave_max_u32(hk == m ? (uint32_t)c[0] : 0u);
     }
     const bool win = (hk == m) && ((uint32_t)c[0] == lo_best);
-    if (lane == slot) {
-      my_idx = min(~lo_best, (uint32_t)(kExperts - 1));  // always a real entry
-      my_key = m;
-    }
+    if (lane == slot) mine = ((uint64_t)m << 32) | lo_best;
     if (win) {
 #pragma unroll
-      for (int i = 0; i < 13; ++i) c[i] = c[i + 1];
-      c[13] = 0;
+      for (int i = 0; i < 15; ++i) c[i] = c[i + 1];
+      c[15] = 0;
     }
   }
+  return mine;
 }
 
-// LDS (uint64 slots) one wave of topk16_wave needs: 64 lane maxima, 64
+// LDS (uint64 slots) one wave of select16 needs: 64 lane maxima, 64
 // candidates + 8 zero pads, 16 selected.
 constexpr int kTopkScratch = 64 + 72 + kTopK;
 
-// One wave selects the 16 largest of a row's 896 logits and writes ids (in
-// selection order) and normalised sigmoid weights. Lane l owns experts l,
-// l + 64, ..., l + 832 as distinct 64-bit keys.
+// One wave selects the 16 largest of a set of distinct 64-bit keys, P per
+// lane (a zero key is padding: it is below every real key). At least 16
+// lanes must hold a real key. Returns, in lane s < 16, the s-th largest key.
 //   1. Threshold: t0 = the 16th largest of the 64 lane maxima; every lane
 //      ranks its maximum against all 64 through LDS. At least 16 keys are
 //      >= t0, so the top 16 are among them.
 //   2. The keys >= t0 (typically about 20) are compacted into LDS in ballot
-//      order; each ranks itself against all of them (keys are distinct), and
-//      rank r < 16 is the r-th selected expert.
-//   3. More than 64 keys >= t0 (the largest logits crowded into a few
-//      lanes) take the sort-and-rounds fallback, which selects the same
-//      experts.
+//      order; each ranks itself against all of them, and rank r < 16 is the
+//      r-th selected key.
+//   3. More than 64 keys >= t0 take the sort-and-rounds fallback, which
+//      selects the same keys.
 // scratch: kTopkScratch uint64 slots of LDS owned by this wave. Waves are
 // independent (no workgroup barrier inside).
-template <bool Coherent = false>
-__device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32_t* __restrict__ ids,
-                                            float* __restrict__ weights, uint64_t* scratch) {
+template <int P>
+__device__ __forceinline__ uint64_t select16(const uint64_t (&c)[P], uint64_t* scratch) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint64_t c[14];
-#pragma unroll
-  for (int i = 0; i < 14; ++i) c[i] = select_key<Coherent>(row, (uint32_t)(i * kWave + lane));
   uint64_t mx = c[0];
 #pragma unroll
-  for (int i = 1; i < 14; ++i) mx = c[i] > mx ? c[i] : mx;
+  for (int i = 1; i < P; ++i) mx = c[i] > mx ? c[i] : mx;
 
   uint64_t* lmax = scratch;
   uint64_t* cand = scratch + 64;
@@ -224,41 +215,42 @@ __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32
     const u64x2 v = *reinterpret_cast<const u64x2*>(lmax + j);
     rk += (v[0] > mx ? 1u : 0u) + (v[1] > mx ? 1u : 0u);
   }
-  // the 64 maxima are distinct, so exactly one lane has rank 15
+  // the real lane maxima are distinct and at least 16 of them rank above
+  // every padding lane, so exactly one lane has rank 15
   const uint64_t t0 = readlane_u64(mx, __builtin_ctzll(ballot(rk == 15u)));
 
   uint32_t n = 0;  // keys >= t0 so far (wave-uniform)
 #pragma unroll
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < P; ++i) {
     const bool p = c[i] >= t0;
     const uint64_t msk = ballot(p);
     const uint32_t pos = n + lanes_below(msk);
     if (p && pos < (uint32_t)kWave) cand[pos] = c[i];
     n += (uint32_t)__builtin_popcountll(msk);
   }
-  uint32_t my_idx, my_key;
-  if (n <= (uint32_t)kWave) {
-    // zero pads up to a multiple of 8: a zero key is below every real key
-    if (lane < 8) cand[n + lane] = 0ull;
-    const uint64_t mine = (uint32_t)lane < n ? cand[lane] : 0ull;
-    uint32_t r = 0;
-    for (uint32_t j = 0; j < n; j += 8) {
+  if (n > (uint32_t)kWave) return select16_rounds<P>(c);
+  // zero pads up to a multiple of 8
+  if (lane < 8) cand[n + lane] = 0ull;
+  const uint64_t mine = (uint32_t)lane < n ? cand[lane] : 0ull;
+  uint32_t r = 0;
+  for (uint32_t j = 0; j < n; j += 8) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) r += cand[j + q] > mine ? 1u : 0u;
-    }
-    if ((uint32_t)lane < n && r < (uint32_t)kTopK) sel[r] = mine;
-    const uint64_t k = lane < kTopK ? sel[lane] : 0ull;
-    my_idx = min(~(uint32_t)k, (uint32_t)(kExperts - 1));
-    my_key = (uint32_t)(k >> 32);
-  } else {
-    topk16_rounds(c, my_idx, my_key);
+    for (int q = 0; q < 8; ++q) r += cand[j + q] > mine ? 1u : 0u;
   }
+  if ((uint32_t)lane < n && r < (uint32_t)kTopK) sel[r] = mine;
+  return lane < kTopK ? sel[lane] : 0ull;
+}
 
-  // Weights: sigmoid in FP64 of the selected logit (recovered from its key),
-  // normalised over the 16 selected (fixed tree).
+// Lanes s < 16 hold the s-th selected key: write the ids (selection order)
+// and the weights, sigmoid in FP64 of the selected logit (recovered from its
+// key) normalised over the 16 in a fixed tree, rounded once to FP32.
+__device__ __forceinline__ void write_selection(uint64_t k, int32_t* __restrict__ ids,
+                                                float* __restrict__ weights) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t my_idx = min(~(uint32_t)k, (uint32_t)(kExperts - 1));
   double s = 0.0;
   if (lane < kTopK) {
-    const double v = (double)key_logit(my_key);
+    const double v = (double)key_logit((uint32_t)(k >> 32));
     s = 1.0 / (1.0 + exp(-v));
   }
   double tot = s;
@@ -268,6 +260,19 @@ __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32
     ids[lane] = (int32_t)my_idx;
     weights[lane] = (float)(s / tot);
   }
+}
+
+// One wave selects the 16 largest of a row's 896 logits and writes ids (in
+// selection order) and normalised sigmoid weights. Lane l owns experts l,
+// l + 64, ..., l + 832 as distinct 64-bit keys.
+template <bool Coherent = false>
+__device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32_t* __restrict__ ids,
+                                            float* __restrict__ weights, uint64_t* scratch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t c[14];
+#pragma unroll
+  for (int i = 0; i < 14; ++i) c[i] = select_key<Coherent>(row, (uint32_t)(i * kWave + lane));
+  write_selection(select16<14>(c, scratch), ids, weights);
 }
 
 }  // namespace route

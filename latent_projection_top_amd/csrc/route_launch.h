@@ -14,8 +14,9 @@ struct DecodeWorkspace {
   double* rt_part;     // [kSplits][rows_cap][896]
 };
 
-size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits);
-size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts);
+size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits,
+                              size_t* off_cand);
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand);
 
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
@@ -24,6 +25,14 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
 
 hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,
                          hipStream_t stream);
+
+// Sharded top-16 (stage 1: local top-16 per expert shard into cand
+// [rows][shards][16] uint64 keys; stage 2: merge). shards divides 896 with at
+// least 16 experts per shard, at most kTopkMaxShards.
+constexpr int kTopkMaxShards = 56;
+bool topk16_shards_valid(int shards);
+hipError_t launch_topk16_sharded(const float* logits, int shards, int32_t* ids, float* weights,
+                                 uint64_t* cand, int rows, hipStream_t stream);
 
 hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
                                  int rows, hipStream_t stream);

@@ -35,7 +35,7 @@ E_HIP = -6
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libroute.so")
 
 SYMBOLS = ("route_prepare", "route_workspace_bytes", "route_latent_router", "route_topk16",
-           "route_fused", "route_destroy", "route_strerror")
+           "route_fused", "route_topk16_sharded", "route_destroy", "route_strerror")
 
 
 class RouteError(RuntimeError):
@@ -66,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.route_topk16.restype = ctypes.c_int
     lib.route_fused.argtypes = [vp, vp, vp, f32p, vp, f32p, i32p, f32p, vp, i32, vp]
     lib.route_fused.restype = ctypes.c_int
+    lib.route_topk16_sharded.argtypes = [vp, f32p, i32, i32p, f32p, vp, i32, vp]
+    lib.route_topk16_sharded.restype = ctypes.c_int
     lib.route_destroy.argtypes = [vp]
     lib.route_destroy.restype = None
     lib.route_strerror.argtypes = [ctypes.c_int]
@@ -170,6 +172,23 @@ def topk16(plan: Plan, logits, ids, weights, rows: int | None = None, stream=Non
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_topk16")
+
+
+def topk16_sharded(plan: Plan, logits, shards: int, ids, weights, workspace, rows: int | None = None,
+                   stream=None) -> None:
+    """Top-16 as a local top-16 per expert shard (896 / shards experts) plus an
+    exact merge; bitwise equal to topk16 on the same logits."""
+    rows = logits.shape[0] if rows is None else rows
+    st = LIB.route_topk16_sharded(
+        ctypes.c_void_p(plan.handle),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        int(shards),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_topk16_sharded")
 
 
 def fused(plan: Plan, x, w_latent, w_router, latent, logits, ids, weights, workspace,

@@ -174,6 +174,32 @@ def topk16_ref(logits: np.ndarray, k: int = TOPK) -> np.ndarray:
     return ids.astype(np.int32)
 
 
+def topk16_sharded_ref(logits: np.ndarray, shards: int, k: int = TOPK) -> np.ndarray:
+    """Top-16 ids as a route whose experts are split over ranks selects them,
+    int32 [rows, 16], in selection order.
+
+    [PR24] "What / why": each row keeps its 16 largest experts; [PR265]: the
+    router output is split by expert over the ranks (56 experts per rank over
+    16 ranks). Step 1: each of `shards` contiguous expert shards keeps its k
+    largest selection keys (global expert numbering). Step 2: the row's k
+    largest among the k * shards candidates, sorted descending. Both steps use
+    a library partition and sort over the same keys as topk16_ref.
+    """
+    logits = np.atleast_2d(logits)
+    rows, e = logits.shape
+    if shards < 1 or e % shards or e // shards < k:
+        raise ValueError("shards must divide the experts with at least k per shard")
+    key = _selection_key(logits)
+    size = e // shards
+    cand = [np.partition(key[:, s * size:(s + 1) * size], size - k, axis=1)[:, size - k:]
+            for s in range(shards)]
+    cand = np.concatenate(cand, axis=1)
+    top = np.partition(cand, cand.shape[1] - k, axis=1)[:, cand.shape[1] - k:]
+    top = np.sort(top, axis=1)[:, ::-1]
+    ids = np.uint64(0xFFFFFFFF) - (top & np.uint64(0xFFFFFFFF))
+    return ids.astype(np.int32)
+
+
 def route_weights_ref(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
     """Normalised sigmoid weights of the selected experts, float32 [rows, 16].
 

@@ -127,5 +127,6 @@ def test_run_calls_reject_null_plan():
     assert route.LIB.route_latent_router(None, None, None, None, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_topk16(None, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_fused(None, None, None, None, None, None, None, None, None, 1, None) == route.E_ARG
+    assert route.LIB.route_topk16_sharded(None, None, 8, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_workspace_bytes(None) == 0
     route.LIB.route_destroy(None)

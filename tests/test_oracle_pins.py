@@ -297,6 +297,48 @@ def test_top16_relabel_experts():
     assert np.array_equal(p[ids2], ids)
 
 
+SHARD_COUNTS = (1, 2, 4, 7, 8, 14, 16, 28, 32, 56)
+
+
+def _clustered_rows(n, seed):
+    """Rows whose largest logits crowd into few expert shards."""
+    r = np.random.default_rng(seed)
+    L = r.standard_normal((n, g.EXPERTS)).astype(np.float32)
+    for i in range(n):
+        s = r.integers(0, 16)
+        L[i, 56 * s:56 * s + 40] += 6.0
+    return L
+
+
+def test_top16_sharded_matches_sorted_on_dense_ties():
+    # tiny value pools (many exact ties, specials) against Python sorted()
+    r = np.random.default_rng(25)
+    pool = np.array([-1.0, -0.0, 0.0, 1.0, 2.0, np.inf, -np.inf, np.nan], dtype=np.float32)
+    L = np.array([r.choice(pool, size=g.EXPERTS, p=[.2, .2, .2, .2, .1, .0, .05, .05])
+                  for _ in range(12)], dtype=np.float32)
+    for shards in SHARD_COUNTS:
+        got = o.topk16_sharded_ref(L, shards)
+        for i in range(L.shape[0]):
+            assert got[i].tolist() == _brute_top16(L[i]), (shards, i)
+
+
+def test_top16_sharded_equals_unsharded():
+    # the merge is exact for every shard count, also when the largest logits
+    # crowd into one shard
+    L = np.concatenate([np.random.default_rng(26).standard_normal((200, g.EXPERTS)).astype(np.float32),
+                        _clustered_rows(100, 27)])
+    ref = o.topk16_ref(L)
+    for shards in SHARD_COUNTS:
+        assert np.array_equal(o.topk16_sharded_ref(L, shards), ref), shards
+
+
+def test_top16_sharded_rejects_bad_shard_counts():
+    L = np.zeros((1, g.EXPERTS), dtype=np.float32)
+    for shards in (0, 3, 5, 64, 112, 896):
+        with pytest.raises(ValueError):
+            o.topk16_sharded_ref(L, shards)
+
+
 def test_top16_near_tie_generator_structure():
     L = g.near_tie_logits(2000, chunk=0)
     ids = o.topk16_ref(L)
