@@ -9,10 +9,11 @@ HBM. Steps are replayed from a HIP graph holding 8 route_fused calls (one per
 weight copy, each on its own input bank); K steps = K/8 replays, timed with
 events on the launch stream between two device synchronisations.
 
-Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows) and
-the 3072-row prefill chunk, the decode kernel's HBM roofline fraction, the
-prefill MFMA fraction, and the CPU oracle timed on this host (a reported
-baseline only).
+Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows), the
+3072-row prefill chunk, the decode kernel at one tensor-parallel rank's share
+(448 x 112 at 8 ranks, 224 x 56 at 16 ranks; 1, 8 and 20 rows), the decode
+kernel's HBM roofline fraction, the prefill MFMA fraction, and the CPU oracle
+timed on this host (a reported baseline only).
 
 Roofline: a decode route is one kernel launch, so the kernel's average launch
 duration is the event-timed graph replay divided by the launches in it (it
@@ -110,18 +111,7 @@ class DecodeSetup:
                     self.ws[i], rows=self.rows)
 
     def capture(self):
-        torch = self.torch
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            self.run_all()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.run_all()
-        torch.cuda.synchronize()
-        return g
+        return capture_graph(self.run_all, self.torch)
 
 
 def time_graph(g, replays: int, torch):
@@ -136,6 +126,57 @@ def time_graph(g, replays: int, torch):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / replays
+
+
+def capture_graph(fn, torch):
+    """fn() run once on a side stream, then captured into a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def share_timings(copies, banks, route, torch, replays: int):
+    """Decode kernel at one tensor-parallel rank's share (latent_router on the
+    rank's contiguous column slices). Every rank's share of every weight copy
+    is a distinct buffer (8 copies x all ranks = 616 MB, more than the
+    Infinity Cache), and one graph replay runs each once."""
+    out = {}
+    for ranks, (lat, exp) in sorted(route.RANK_SHARES.items()):
+        shares = [(w[:, r * lat:(r + 1) * lat].contiguous(), wr[:, r * exp:(r + 1) * exp].contiguous())
+                  for w, wr in copies for r in range(ranks)]
+        share_bytes = K * (lat * 2 + exp * 4)
+        for rows in (1, 8, 20):
+            plan = route.Plan(route.MODE_DECODE, rows, latent=lat, experts=exp)
+            ws = plan.new_workspace()
+            xs = [banks[i % len(banks)][:rows].contiguous() for i in range(len(shares))]
+            lat_o = torch.empty((rows, lat), dtype=torch.bfloat16, device="cuda")
+            lg_o = torch.empty((rows, exp), dtype=torch.float32, device="cuda")
+
+            def run():
+                for i, (w, wr) in enumerate(shares):
+                    route.latent_router(plan, xs[i], w, wr, lat_o, lg_o, ws, rows=rows)
+
+            g = capture_graph(run, torch)
+            for _ in range(2):
+                g.replay()
+            us = time_graph(g, replays, torch) * 1000.0 / len(shares)
+            nbytes = share_bytes + rows * (K * 2 + lat * 2 + exp * 4)
+            out[f"{ranks}x{rows}"] = {"ranks": ranks, "latent": lat, "experts": exp, "rows": rows,
+                                      "us": round(us, 3),
+                                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            log(f"share {ranks} ranks ({lat}x{exp}) rows={rows}: {us:.2f} us per launch "
+                f"({nbytes / us / 1e3:.0f} GB/s)")
+            del g
+        del shares
+    return out
 
 
 def profile_pass(rows: int, copies, banks, route, torch):
@@ -251,7 +292,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "decode_route_kernel<1>" if args.rows <= 16 else "decode_route_kernel<2>",
+                "kernel": f"decode_route_kernel<{1 if args.rows <= 16 else 2}, DecodeShape<3584, 896, 4, 16>>",
                 "kernel_us_per_launch": round(kernel_ms * 1000.0, 3),
                 "algorithmic_bytes_per_launch": decode_bytes(args.rows)}
 
@@ -294,6 +335,10 @@ def main():
         log(f"prefill 3072: {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
             f"{t_lr:.1f} us = {prefill['mfma_tflops']} TFLOP/s, top-16 {t_tk:.1f} us")
 
+    shares = None
+    if not args.no_extras:
+        shares = share_timings(copies, banks, route, torch, replays=20)
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle ...")
@@ -329,6 +374,7 @@ def main():
         "decode_hbm_frac_by_rows": {str(k): round(decode_bytes(k) / (v * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
                                     for k, v in sorted(results.items())},
         "prefill": prefill,
+        "rank_share_decode": shares,
     }
     print(json.dumps(out), flush=True)
 

@@ -46,6 +46,22 @@
  *   ids      [rows][16]     int32, selection order
  *   weights  [rows][16]     FP32, same order as ids
  *
+ * Rank shares (decode only): a decode plan may instead be prepared for one
+ * tensor-parallel rank's share of the route, latent x experts = 448 x 112 (8
+ * ranks) or 224 x 56 (16 ranks): the per-rank output shapes of page "Use two
+ * row blocks for eight-row Kimi paired gathers" (BF16 [8, 224] latent and FP32
+ * [8, 56] router at 16 ranks) and of page "Optionally gather the Kimi3 prefill
+ * latent instead of reducing it" (448 latent columns per rank at 8 ranks).
+ * Every 3584 and 896 above then reads as the share's latent and experts:
+ * w_latent [7168][latent] and w_router [7168][experts] are the rank's
+ * contiguous column slices of the full weights (copied out by the caller),
+ * and latent/logits have that many columns. Each output is still one full-K
+ * dot product rounded once, within the same bounds as the whole route's (the
+ * K split differs, so the last bit may differ from the whole route's
+ * corresponding column). A share has no top-16
+ * (its experts are a fraction of the route's): route_topk16, route_fused and
+ * route_topk16_sharded return ROUTE_E_SHAPE on a share plan.
+ *
  * `stream` is a hipStream_t (NULL = the null stream); the current HIP device
  * must be the plan's device.
  */
@@ -71,7 +87,9 @@ extern "C" {
 #define ROUTE_OK 0
 #define ROUTE_E_ARG (-1)    /* NULL pointer, bad abi_version or unknown mode */
 #define ROUTE_E_ROWS (-2)   /* rows outside the mode's envelope, or above the plan's */
-#define ROUTE_E_SHAPE (-3)  /* hidden/latent/experts/topk differ from 7168/3584/896/16 */
+#define ROUTE_E_SHAPE (-3)  /* hidden/topk not 7168/16, latent x experts not 3584 x 896
+                               (or a decode share 448 x 112 / 224 x 56), or a
+                               top-16 call on a share plan */
 #define ROUTE_E_ALIGN (-4)  /* a device pointer is not 16-byte aligned */
 #define ROUTE_E_DEVICE (-5) /* no such device, not gfx950, or not the current device */
 #define ROUTE_E_HIP (-6)    /* the HIP runtime rejected a launch */
@@ -83,8 +101,8 @@ typedef struct {
   int32_t mode;         /* route_mode */
   int32_t rows;         /* the most rows any call on this plan passes */
   int32_t hidden;       /* 7168 */
-  int32_t latent;       /* 3584 */
-  int32_t experts;      /* 896 */
+  int32_t latent;       /* 3584; decode shares: 448 or 224 */
+  int32_t experts;      /* 896; decode shares: 112 or 56 (with 448 / 224) */
   int32_t topk;         /* 16 */
   int32_t device;       /* HIP device ordinal */
 } route_config;
@@ -107,7 +125,8 @@ int route_latent_router(const route_plan* plan, const void* x, const void* w_lat
                         const float* w_router, void* latent, float* logits,
                         void* workspace, int32_t rows, void* stream);
 
-/* Standalone top-16 of `rows` rows of FP32 logits (1..plan rows). */
+/* Standalone top-16 of `rows` rows of FP32 logits (1..plan rows). A share
+ * plan returns ROUTE_E_SHAPE. */
 int route_topk16(const route_plan* plan, const float* logits, int32_t* ids,
                  float* weights, int32_t rows, void* stream);
 

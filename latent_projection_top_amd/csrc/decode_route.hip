@@ -45,44 +45,66 @@ namespace route {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;              // 256
-
-// latent units
-constexpr int kSplitsL = 4;
-constexpr int kKL = kHidden / kSplitsL;               // 1792 rows per unit
-constexpr int kKLWave = kKL / kWaves;                 // 448 rows per wave
-constexpr int kStepL = 32;
-constexpr int kStepsL = kKLWave / kStepL;             // 14
-constexpr int kLatTileN = 64;
-constexpr int kLatTiles = kLatent / kLatTileN;        // 56
-constexpr int kLatUnits = kLatTiles * kSplitsL;       // 224
-
-// router units
-constexpr int kSplitsR = 16;
-constexpr int kKR = kHidden / kSplitsR;               // 448 rows per unit
-constexpr int kKRWave = kKR / kWaves;                 // 112 rows per wave
-constexpr int kStepR = 16;
-constexpr int kStepsR = kKRWave / kStepR;             // 7
-constexpr int kRtTileE = 32;
-constexpr int kRtTiles = kExperts / kRtTileE;         // 28
-constexpr int kRtUnits = kRtTiles * kSplitsR;         // 448
-
-constexpr int kGrid = kRtUnits + kLatUnits;           // 672: one workgroup per unit
+constexpr int kStepL = 32;                            // latent rows per MFMA step
+constexpr int kLatTileN = 64;                         // latent columns per unit
+constexpr int kStepR = 16;                            // router rows per step
+constexpr int kRtTileE = 32;                          // experts per router unit
 constexpr int kDecodeMaxRows = 20;
 constexpr int kRowGroup = kWaves;                     // rows selected together, one per wave
 
-// Workspace counters (uint32). Every counter is shared by few workgroups:
-// atomics on one address from hundreds of workgroups serialise.
-constexpr int kCtrRtTile = kLatTiles;                 // [28] router units stored per tile
-constexpr int kCtrRouter = kLatTiles + kRtTiles;      // router tiles combined
-constexpr int kCtrRows = kCtrRouter + 1;              // rows claimed
-constexpr int kCtrFin = kCtrRouter + 2;               // row-phase participants finished
-constexpr int kDecodeCounters = kCtrRouter + 3;
-// Row-phase participants: the workgroup that combines the last router tile and
-// the 56 workgroups that combine a latent tile, each exactly once per call.
-constexpr int kRowParticipants = 1 + kLatTiles;
-
-static_assert(kKLWave % kStepL == 0 && kKRWave % kStepR == 0, "whole steps per wave");
-static_assert(kLatent % kLatTileN == 0 && kExperts % kRtTileE == 0, "tiles");
+// Output shape of one launch: the whole route (N = 3584 latent columns, E =
+// 896 experts), or one tensor-parallel rank's share of it, whose weights are
+// the rank's contiguous column slices: N = 448, E = 112 at 8 ranks; N = 224,
+// E = 56 at 16 ranks (page "Optionally gather the Kimi3 prefill latent
+// instead of reducing it", Description: 448 latent columns per rank; page "Use
+// two row blocks for eight-row Kimi paired gathers": BF16 [8, 224] latent and
+// FP32 [8, 56] router output per rank). A share has a few MB
+// of weights, so it splits K further to spread them over the CUs; partial
+// tiles at the end of a share are masked.
+template <int N_, int E_, int SplitsL_, int SplitsR_>
+struct DecodeShape {
+  static constexpr int N = N_;                        // row stride of W, latent columns
+  static constexpr int E = E_;                        // row stride of Wr, experts
+  static constexpr bool kFull = N == kLatent && E == kExperts;
+  // latent units: column tile x K split
+  static constexpr int SplitsL = SplitsL_;
+  static constexpr int KL = kHidden / SplitsL;        // rows per unit (1792 whole)
+  static constexpr int KLWave = KL / kWaves;          // rows per wave (448)
+  static constexpr int StepsL = KLWave / kStepL;      // MFMA steps per wave (14)
+  static constexpr int LatTiles = (N + kLatTileN - 1) / kLatTileN;
+  static constexpr int LatUnits = LatTiles * SplitsL;
+  // router units: expert tile x K split
+  static constexpr int SplitsR = SplitsR_;
+  static constexpr int KR = kHidden / SplitsR;        // rows per unit (448 whole)
+  static constexpr int KRWave = KR / kWaves;          // rows per wave (112)
+  static constexpr int StepsR = KRWave / kStepR;      // MFMA steps per wave (7)
+  static constexpr int RtTiles = (E + kRtTileE - 1) / kRtTileE;
+  static constexpr int RtUnits = RtTiles * SplitsR;
+  static constexpr int Grid = RtUnits + LatUnits;     // one workgroup per unit
+  // Workspace counters (uint32). Every counter is shared by few workgroups:
+  // atomics on one address from hundreds of workgroups serialise.
+  static constexpr int CtrRtTile = LatTiles;          // router units stored per tile
+  static constexpr int CtrRouter = LatTiles + RtTiles;  // router tiles combined
+  static constexpr int CtrRows = CtrRouter + 1;       // rows claimed
+  static constexpr int CtrFin = CtrRouter + 2;        // row-phase participants finished
+  static constexpr int Counters = CtrRouter + 3;
+  // Row-phase participants: the workgroup that combines the last router tile
+  // and the workgroups that combine a latent tile, each once per call.
+  static constexpr int RowParticipants = 1 + LatTiles;
+  static_assert(KL * SplitsL == kHidden && KR * SplitsR == kHidden, "the splits cover K");
+  static_assert(KLWave % kStepL == 0 && KRWave % kStepR == 0, "whole steps per wave");
+  static_assert(N % 4 == 0 && E % 2 == 0, "a lane's loads stay inside a row");
+};
+using FullShape = DecodeShape<kLatent, kExperts, 4, 16>;
+// Share splits measured on MI355X (graph-replayed launches over 616 MB of
+// distinct shares): with the tile combine's loads all in flight, fewer and
+// longer K chunks won over 28 latent / 56 router splits by 1.5 to 3 us.
+using Tp8Shape = DecodeShape<448, 112, 7, 28>;
+using Tp16Shape = DecodeShape<224, 56, 14, 28>;
+constexpr int kDecodeCounters = FullShape::Counters;   // the largest counter set
+static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters,
+              "every shape's counters fit the workspace's counter area");
+static_assert(FullShape::LatTiles == 56 && FullShape::RtTiles == 28 && FullShape::Grid == 672, "full shape");
 
 // Rows a workgroup keeps in its LDS reduction buffer: the MFMA pads rows to 16
 // or 32, but only real rows (at most 20) are stored.
@@ -94,6 +116,16 @@ constexpr int rows_kept() { return NT == 1 ? 16 : kDecodeMaxRows; }
 template <int NT>
 constexpr int depth() { return NT == 1 ? 4 : 3; }
 
+// Outputs per thread whose partials one tile combine loads together: enough
+// for every output the thread has (the most rows of the variant times the
+// tile width, over the workgroup's threads), within `budget` loaded values.
+template <int NT, int TileW>
+constexpr int combine_batch(int splits, int budget) {
+  const int need = ((NT == 1 ? 16 : kDecodeMaxRows) * TileW + kThreads - 1) / kThreads;
+  const int fit = budget / splits > 0 ? budget / splits : 1;
+  return need < fit ? need : fit;
+}
+
 struct DecodeArgs {
   const uint16_t* __restrict__ x;
   const uint16_t* __restrict__ w;
@@ -102,8 +134,8 @@ struct DecodeArgs {
   float* __restrict__ logits;
   int32_t* __restrict__ ids;
   float* __restrict__ weights;
-  float* __restrict__ lat_part;   // [kSplitsL][rows_cap][N]
-  double* __restrict__ rt_part;   // [kSplitsR][rows_cap][E]
+  float* __restrict__ lat_part;   // [SplitsL][rows_cap][N]
+  double* __restrict__ rt_part;   // [SplitsR][rows_cap][E]
   uint32_t* __restrict__ counters;
   int rows;
   int rows_cap;
@@ -166,7 +198,7 @@ __device__ __forceinline__ void hidden_rows(const DecodeArgs& a, int m, int (&xr
 
 // Returns true in the workgroup that combined the last router tile: every
 // logit of every row is then stored.
-template <int NT>
+template <int NT, class Sh>
 __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -176,25 +208,27 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   int xr[NT];
   hidden_rows<NT>(a, m, xr);
 
-  const int tile = u % kRtTiles;
-  const int split = u / kRtTiles;
+  const int tile = u % Sh::RtTiles;
+  const int split = u / Sh::RtTiles;
   const int e0 = tile * kRtTileE;
-  const int k0 = split * kKR + wave * kKRWave;
-  const float* wp = a.wr + (size_t)(k0 + 4 * g) * kExperts + e0 + 2 * m;
+  const int k0 = split * Sh::KR + wave * Sh::KRWave;
+  // lanes past the last expert of a share read a valid pair; never stored
+  const int ecol = Sh::E % kRtTileE == 0 ? e0 + 2 * m : min(e0 + 2 * m, Sh::E - 2);
+  const float* wp = a.wr + (size_t)(k0 + 4 * g) * Sh::E + ecol;
 
   f64x4 acc[NT][2];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 2; ++c) acc[nt][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-  constexpr int kDepthR = 4;
+  constexpr int kDepthR = Sh::StepsR < 4 ? Sh::StepsR : 4;
   f32x2 wv[kDepthR][4];
   u32x2 xv[kDepthR][NT];
   auto issue = [&](int st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       wv[st % kDepthR][j] =
-          __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStepR + j) * kExperts));
+          __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStepR + j) * Sh::E));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       xv[st % kDepthR][nt] = *(const u32x2*)(a.x + (size_t)xr[nt] * kHidden + k0 + 4 * g + st * kStepR);
@@ -203,7 +237,7 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int st = 0; st < kDepthR; ++st) issue(st);
   __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
 #pragma unroll
-  for (int st = 0; st < kStepsR; ++st) {
+  for (int st = 0; st < Sh::StepsR; ++st) {
     const int q = st % kDepthR;
     // lane (g, m) at step j: A[m][g] = Wr[k][e0 + 2m + c], B[g][m] = x[row m][k],
     // k = k0 + 16*st + 4*g + j
@@ -218,7 +252,7 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
         acc[nt][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w1, xd, acc[nt][1], 0, 0, 0);
       }
     }
-    if (st + kDepthR < kStepsR) issue(st + kDepthR);
+    if (st + kDepthR < Sh::StepsR) issue(st + kDepthR);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -241,27 +275,44 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
     double s = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) s += red[(w * kRowsPad + r) * kRtTileE + e];
-    st_dev(&a.rt_part[((size_t)split * a.rows_cap + r) * kExperts + e0 + e], s);
+    if (Sh::E % kRtTileE == 0 || e0 + e < Sh::E)
+      st_dev(&a.rt_part[((size_t)split * a.rows_cap + r) * Sh::E + e0 + e], s);
   }
-  if (publish(&a.counters[kCtrRtTile + tile], slot) != (uint32_t)(kSplitsR - 1)) return false;
-  // last unit of this tile: the tile's logits from its 16 partials
-  for (int i = threadIdx.x; i < outs; i += kThreads) {
-    const int r = i / kRtTileE;
-    const int e = i % kRtTileE;
-    double p[kSplitsR];
+  if (publish(&a.counters[Sh::CtrRtTile + tile], slot) != (uint32_t)(Sh::SplitsR - 1)) return false;
+  // Last unit of this tile: each logit is the sum of its partials in split
+  // order. Every coherent load is a round trip to memory, so a thread loads
+  // the partials of all its outputs (up to 48 values) before adding any.
+  constexpr int kJB = combine_batch<NT, kRtTileE>(Sh::SplitsR, 48);
+  for (int i0 = threadIdx.x; i0 < outs; i0 += kJB * kThreads) {
+    double p[kJB][Sh::SplitsR];
 #pragma unroll
-    for (int sp = 0; sp < kSplitsR; ++sp)
-      p[sp] = ld_dev(&a.rt_part[((size_t)sp * a.rows_cap + r) * kExperts + e0 + e]);
-    double s = 0.0;
+    for (int j = 0; j < kJB; ++j) {
+      // past the last output or expert: load a valid partial, store nothing
+      const int i = min(i0 + j * kThreads, outs - 1);
+      const int r = i / kRtTileE;
+      const int e = min(e0 + i % kRtTileE, Sh::E - 1);
 #pragma unroll
-    for (int sp = 0; sp < kSplitsR; ++sp) s += p[sp];
-    st_dev(&a.logits[(size_t)r * kExperts + e0 + e], (float)s);
+      for (int q = 0; q < Sh::SplitsR; ++q)
+        p[j][q] = ld_dev(&a.rt_part[((size_t)q * a.rows_cap + r) * Sh::E + e]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first add
+#pragma unroll
+    for (int j = 0; j < kJB; ++j) {
+      const int i = i0 + j * kThreads;
+      const int r = i / kRtTileE;
+      const int e = e0 + i % kRtTileE;
+      if (i >= outs || (Sh::E % kRtTileE != 0 && e >= Sh::E)) continue;
+      double s = 0.0;
+#pragma unroll
+      for (int q = 0; q < Sh::SplitsR; ++q) s += p[j][q];
+      st_dev(&a.logits[(size_t)r * Sh::E + e], (float)s);
+    }
   }
-  if (threadIdx.x == 0) st_dev(&a.counters[kCtrRtTile + tile], 0u);
-  return publish(&a.counters[kCtrRouter], slot) == (uint32_t)(kRtTiles - 1);
+  if (threadIdx.x == 0) st_dev(&a.counters[Sh::CtrRtTile + tile], 0u);
+  return publish(&a.counters[Sh::CtrRouter], slot) == (uint32_t)(Sh::RtTiles - 1);
 }
 
-template <int NT>
+template <int NT, class Sh>
 __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -271,25 +322,27 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   int xr[NT];
   hidden_rows<NT>(a, m, xr);
 
-  const int tile = u % kLatTiles;
-  const int split = u / kLatTiles;
+  const int tile = u % Sh::LatTiles;
+  const int split = u / Sh::LatTiles;
   const int n0 = tile * kLatTileN;
-  const int k0 = split * kKL + wave * kKLWave;
-  const uint16_t* wp = a.w + (size_t)(k0 + 8 * g) * kLatent + n0 + 4 * m;
+  const int k0 = split * Sh::KL + wave * Sh::KLWave;
+  // lanes past the last column of a share read a valid quad; never stored
+  const int ncol = Sh::N % kLatTileN == 0 ? n0 + 4 * m : min(n0 + 4 * m, Sh::N - 4);
+  const uint16_t* wp = a.w + (size_t)(k0 + 8 * g) * Sh::N + ncol;
 
   f32x4 acc[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kDepth = depth<NT>();
+  constexpr int kDepth = depth<NT>() < Sh::StepsL ? depth<NT>() : Sh::StepsL;
   u32x2 wv[kDepth][8];
   u32x4 xv[kDepth][NT];
   auto issue = [&](int st) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       wv[st % kDepth][j] =
-          __builtin_nontemporal_load((const u32x2*)(wp + (size_t)(st * kStepL + j) * kLatent));
+          __builtin_nontemporal_load((const u32x2*)(wp + (size_t)(st * kStepL + j) * Sh::N));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       xv[st % kDepth][nt] = *(const u32x4*)(a.x + (size_t)xr[nt] * kHidden + k0 + 8 * g + st * kStepL);
@@ -298,7 +351,7 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int st = 0; st < kDepth; ++st) issue(st);
   __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
 #pragma unroll
-  for (int st = 0; st < kStepsL; ++st) {
+  for (int st = 0; st < Sh::StepsL; ++st) {
     const int q = st % kDepth;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -312,7 +365,7 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
         acc[nt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv[q][nt]), acc[nt][c], 0, 0, 0);
     }
-    if (st + kDepth < kStepsL) issue(st + kDepth);
+    if (st + kDepth < Sh::StepsL) issue(st + kDepth);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -334,20 +387,38 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
     double s = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) s += (double)red[(w * kRowsPad + r) * kLatTileN + col];
-    st_dev(&a.lat_part[((size_t)split * a.rows_cap + r) * kLatent + n0 + col], (float)s);
+    if (Sh::N % kLatTileN == 0 || n0 + col < Sh::N)
+      st_dev(&a.lat_part[((size_t)split * a.rows_cap + r) * Sh::N + n0 + col], (float)s);
   }
-  if (publish(&a.counters[tile], slot) != (uint32_t)(kSplitsL - 1)) return false;
-  for (int i = threadIdx.x; i < outs; i += kThreads) {
-    const int r = i / kLatTileN;
-    const int col = i % kLatTileN;
-    float p[kSplitsL];
+  if (publish(&a.counters[tile], slot) != (uint32_t)(Sh::SplitsL - 1)) return false;
+  // Last unit of this tile: the partials in split order, summed in FP64 and
+  // rounded once; a thread loads the partials of all its outputs (up to 32
+  // values) before adding any.
+  constexpr int kJB = combine_batch<NT, kLatTileN>(Sh::SplitsL, 32);
+  for (int i0 = threadIdx.x; i0 < outs; i0 += kJB * kThreads) {
+    float p[kJB][Sh::SplitsL];
 #pragma unroll
-    for (int sp = 0; sp < kSplitsL; ++sp)
-      p[sp] = ld_dev(&a.lat_part[((size_t)sp * a.rows_cap + r) * kLatent + n0 + col]);
-    double s = 0.0;
+    for (int j = 0; j < kJB; ++j) {
+      // past the last output or column: load a valid partial, store nothing
+      const int i = min(i0 + j * kThreads, outs - 1);
+      const int r = i / kLatTileN;
+      const int n = min(n0 + i % kLatTileN, Sh::N - 1);
 #pragma unroll
-    for (int sp = 0; sp < kSplitsL; ++sp) s += (double)p[sp];
-    a.latent[(size_t)r * kLatent + n0 + col] = f64_to_bf16_rne(s);
+      for (int q = 0; q < Sh::SplitsL; ++q)
+        p[j][q] = ld_dev(&a.lat_part[((size_t)q * a.rows_cap + r) * Sh::N + n]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first add
+#pragma unroll
+    for (int j = 0; j < kJB; ++j) {
+      const int i = i0 + j * kThreads;
+      const int r = i / kLatTileN;
+      const int n = n0 + i % kLatTileN;
+      if (i >= outs || (Sh::N % kLatTileN != 0 && n >= Sh::N)) continue;
+      double s = 0.0;
+#pragma unroll
+      for (int q = 0; q < Sh::SplitsL; ++q) s += (double)p[j][q];
+      a.latent[(size_t)r * Sh::N + n] = f64_to_bf16_rne(s);
+    }
   }
   if (threadIdx.x == 0) st_dev(&a.counters[tile], 0u);
   return true;
@@ -372,24 +443,26 @@ __device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
 // which starts on it without a claim; the counter hands out the later groups.
 // Returns the group's first row, or -1 when the router phase is not complete
 // or no row is left. `router_done` is thread 0's knowledge that it is complete.
+template <class Sh>
 __device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done, int* slot) {
   int r = -1;
   if (threadIdx.x == 0) {
-    if (router_done || ld_dev(&a.counters[kCtrRouter]) == (uint32_t)kRtTiles) {
-      const uint32_t c = kRowGroup + add_dev(&a.counters[kCtrRows], (uint32_t)kRowGroup);
+    if (router_done || ld_dev(&a.counters[Sh::CtrRouter]) == (uint32_t)Sh::RtTiles) {
+      const uint32_t c = kRowGroup + add_dev(&a.counters[Sh::CtrRows], (uint32_t)kRowGroup);
       if (c < (uint32_t)a.rows) r = (int)c;
     }
   }
   return broadcast(r, slot);
 }
 
-// Workgroup b < 448 runs router unit b, the others latent unit b - 448. Row
-// groups (the fused top-16) are taken by the workgroup that combines the last
-// router tile, until none is left, and by every workgroup that combines a
-// latent tile, if the logits are complete by then. These 57 participants each
-// bump kCtrFin once when they stop taking rows; the last resets the row-phase
-// counters for the next call.
-template <int NT>
+// Workgroup b < Sh::RtUnits (448 for the whole route) runs router unit b, the
+// others latent unit b - Sh::RtUnits. Row groups (the fused top-16) are taken
+// by the workgroup that combines the last router tile, until none is left, and
+// by every workgroup that combines a latent tile, if the logits are complete by
+// then. These participants (57 for the whole route) each bump CtrFin once when
+// they stop taking rows; the last resets the row-phase counters for the next
+// call.
+template <int NT, class Sh>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_route_kernel(DecodeArgs a) {
   constexpr int kLatBytes = kWaves * rows_kept<NT>() * kLatTileN * 4;
@@ -402,43 +475,76 @@ void decode_route_kernel(DecodeArgs a) {
 
   const int b = blockIdx.x;
   bool router_done = false;
-  if (b < kRtUnits) {
-    router_done = router_unit<NT>(a, b, smem, &slot);
+  if (b < Sh::RtUnits) {
+    router_done = router_unit<NT, Sh>(a, b, smem, &slot);
     if (!router_done) return;
-  } else if (!latent_unit<NT>(a, b - kRtUnits, smem, &slot)) {
+  } else if (!latent_unit<NT, Sh>(a, b - Sh::RtUnits, smem, &slot)) {
+    return;
+  }
+  if constexpr (!Sh::kFull) {
+    // A share has no row phase (its experts are a fraction of the route's, so
+    // there is nothing to select): the workgroup that combined the last router
+    // tile resets the router counter, and the call ends.
+    if (router_done && threadIdx.x == 0) st_dev(&a.counters[Sh::CtrRouter], 0u);
     return;
   }
   if (router_done) row_group(a, 0, smem);
-  for (int r = claim_rows(a, router_done, &slot); r >= 0; r = claim_rows(a, router_done, &slot))
+  for (int r = claim_rows<Sh>(a, router_done, &slot); r >= 0; r = claim_rows<Sh>(a, router_done, &slot))
     row_group(a, r, smem);
-  if (publish(&a.counters[kCtrFin], &slot) == (uint32_t)(kRowParticipants - 1) && threadIdx.x == 0) {
-    st_dev(&a.counters[kCtrRouter], 0u);
-    st_dev(&a.counters[kCtrRows], 0u);
-    st_dev(&a.counters[kCtrFin], 0u);
+  if (publish(&a.counters[Sh::CtrFin], &slot) == (uint32_t)(Sh::RowParticipants - 1) && threadIdx.x == 0) {
+    st_dev(&a.counters[Sh::CtrRouter], 0u);
+    st_dev(&a.counters[Sh::CtrRows], 0u);
+    st_dev(&a.counters[Sh::CtrFin], 0u);
   }
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits,
-                              size_t* off_cand) {
+template <class Sh>
+static size_t ws_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits, size_t* off_cand) {
   size_t off = align256(sizeof(uint32_t) * kDecodeCounters);
   *off_lat = off;
-  off = align256(off + sizeof(float) * kSplitsL * (size_t)rows_cap * kLatent);
+  off = align256(off + sizeof(float) * Sh::SplitsL * (size_t)rows_cap * Sh::N);
   *off_rt = off;
-  off = align256(off + sizeof(double) * kSplitsR * (size_t)rows_cap * kExperts);
+  off = align256(off + sizeof(double) * Sh::SplitsR * (size_t)rows_cap * Sh::E);
   *off_logits = off;
-  off = align256(off + sizeof(float) * (size_t)rows_cap * kExperts);
+  off = align256(off + sizeof(float) * (size_t)rows_cap * Sh::E);
   *off_cand = off;
   off = align256(off + sizeof(uint64_t) * (size_t)rows_cap * kTopkMaxShards * kTopK);
   return off;
 }
 
+bool decode_shape_valid(int latent, int experts) {
+  return (latent == FullShape::N && experts == FullShape::E) ||
+         (latent == Tp8Shape::N && experts == Tp8Shape::E) ||
+         (latent == Tp16Shape::N && experts == Tp16Shape::E);
+}
+
+size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off_lat, size_t* off_rt,
+                              size_t* off_logits, size_t* off_cand) {
+  if (latent == Tp8Shape::N && experts == Tp8Shape::E)
+    return ws_bytes<Tp8Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
+  if (latent == Tp16Shape::N && experts == Tp16Shape::E)
+    return ws_bytes<Tp16Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
+  return ws_bytes<FullShape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
+}
+
+template <class Sh>
+static void launch_shape(const DecodeArgs& a, int rows, hipStream_t stream) {
+  if (rows <= 16)
+    hipLaunchKernelGGL((decode_route_kernel<1, Sh>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_route_kernel<2, Sh>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
+}
+
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
-                               const DecodeWorkspace& ws, int rows, int rows_cap, bool fuse_topk,
-                               hipStream_t stream) {
+                               const DecodeWorkspace& ws, int rows, int rows_cap, int n_latent,
+                               int n_experts, bool fuse_topk, hipStream_t stream) {
   if (rows < 1 || rows > kDecodeMaxRows || rows > rows_cap) return hipErrorInvalidValue;
+  if (!decode_shape_valid(n_latent, n_experts)) return hipErrorInvalidValue;
+  const bool full = n_latent == FullShape::N;
+  if (fuse_topk && !full) return hipErrorInvalidValue;
   DecodeArgs a;
   a.x = x;
   a.w = w_latent;
@@ -453,10 +559,12 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (rows <= 16)
-    hipLaunchKernelGGL(decode_route_kernel<1>, dim3(kGrid), dim3(kThreads), 0, stream, a);
+  if (full)
+    launch_shape<FullShape>(a, rows, stream);
+  else if (n_latent == Tp8Shape::N)
+    launch_shape<Tp8Shape>(a, rows, stream);
   else
-    hipLaunchKernelGGL(decode_route_kernel<2>, dim3(kGrid), dim3(kThreads), 0, stream, a);
+    launch_shape<Tp16Shape>(a, rows, stream);
   return hipGetLastError();
 }
 

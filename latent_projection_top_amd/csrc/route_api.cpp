@@ -14,6 +14,8 @@ struct route_plan {
   int32_t mode;
   int32_t rows_cap;
   int32_t device;
+  int32_t latent;     // output shape: the whole route or one rank's share
+  int32_t experts;
   size_t ws_bytes;
   size_t off_lat;     // decode: latent partials
   size_t off_rt;      // decode: router partials
@@ -36,6 +38,10 @@ int check_rows(const route_plan* p, int32_t rows) {
   return (rows < 1 || rows > p->rows_cap) ? ROUTE_E_ROWS : ROUTE_OK;
 }
 
+// A share plan (one tensor-parallel rank's columns) has no top-16: its
+// experts are a fraction of the route's.
+bool is_share(const route_plan* p) { return p->latent != ROUTE_LATENT || p->experts != ROUTE_EXPERTS; }
+
 int status_of(hipError_t e) { return e == hipSuccess ? ROUTE_OK : ROUTE_E_HIP; }
 
 route::DecodeWorkspace decode_ws(const route_plan* p, void* ws) {
@@ -56,7 +62,8 @@ int run_latent_router(const route_plan* p, const void* x, const void* w_latent, 
   if (p->mode == ROUTE_MODE_DECODE) {
     // decode: one launch; the fused select runs inside the projection kernel
     return status_of(route::launch_decode_route(xb, wb, w_router, lb, logits, ids, weights,
-                                                decode_ws(p, ws), rows, p->rows_cap, fused, s));
+                                                decode_ws(p, ws), rows, p->rows_cap, p->latent,
+                                                p->experts, fused, s));
   }
   int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, s));
   if (st != ROUTE_OK) return st;
@@ -75,8 +82,11 @@ int route_prepare(const route_config* cfg, route_plan** out) {
   *out = nullptr;
   if (cfg == nullptr || cfg->abi_version != ROUTE_ABI_VERSION) return ROUTE_E_ARG;
   if (cfg->mode != ROUTE_MODE_DECODE && cfg->mode != ROUTE_MODE_PREFILL) return ROUTE_E_ARG;
-  if (cfg->hidden != ROUTE_HIDDEN || cfg->latent != ROUTE_LATENT || cfg->experts != ROUTE_EXPERTS ||
-      cfg->topk != ROUTE_TOPK)
+  if (cfg->hidden != ROUTE_HIDDEN || cfg->topk != ROUTE_TOPK ||
+      !route::decode_shape_valid(cfg->latent, cfg->experts))
+    return ROUTE_E_SHAPE;
+  // rank shares are decode-only
+  if (cfg->mode != ROUTE_MODE_DECODE && (cfg->latent != ROUTE_LATENT || cfg->experts != ROUTE_EXPERTS))
     return ROUTE_E_SHAPE;
   const int32_t max_rows = cfg->mode == ROUTE_MODE_DECODE ? ROUTE_DECODE_MAX_ROWS : ROUTE_PREFILL_MAX_ROWS;
   if (cfg->rows < 1 || cfg->rows > max_rows) return ROUTE_E_ROWS;
@@ -93,9 +103,11 @@ int route_prepare(const route_config* cfg, route_plan** out) {
   p->mode = cfg->mode;
   p->rows_cap = cfg->rows;
   p->device = cfg->device;
+  p->latent = cfg->latent;
+  p->experts = cfg->experts;
   if (p->mode == ROUTE_MODE_DECODE) {
-    p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, &p->off_lat, &p->off_rt, &p->off_logits,
-                                                &p->off_cand);
+    p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, p->latent, p->experts, &p->off_lat,
+                                                &p->off_rt, &p->off_logits, &p->off_cand);
     p->off_parts = 0;
   } else {
     p->off_lat = p->off_rt = 0;
@@ -123,6 +135,7 @@ int route_latent_router(const route_plan* plan, const void* x, const void* w_lat
 int route_topk16(const route_plan* plan, const float* logits, int32_t* ids, float* weights,
                  int32_t rows, void* stream) {
   if (!plan || !logits || !ids || !weights) return ROUTE_E_ARG;
+  if (is_share(plan)) return ROUTE_E_SHAPE;
   if (int st = check_rows(plan, rows)) return st;
   if (misaligned(logits) || misaligned(ids) || misaligned(weights)) return ROUTE_E_ALIGN;
   if (int st = check_device(plan)) return st;
@@ -134,6 +147,7 @@ int route_fused(const route_plan* plan, const void* x, const void* w_latent, con
                 int32_t rows, void* stream) {
   if (!plan || !x || !w_latent || !w_router || !latent || !ids || !weights || !workspace)
     return ROUTE_E_ARG;
+  if (is_share(plan)) return ROUTE_E_SHAPE;
   if (int st = check_rows(plan, rows)) return st;
   if (misaligned(x) || misaligned(w_latent) || misaligned(w_router) || misaligned(latent) ||
       (logits && misaligned(logits)) || misaligned(ids) || misaligned(weights) || misaligned(workspace))
@@ -149,6 +163,7 @@ int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t sh
                          float* weights, void* workspace, int32_t rows, void* stream) {
   if (!plan || !logits || !ids || !weights || !workspace) return ROUTE_E_ARG;
   if (!route::topk16_shards_valid(shards)) return ROUTE_E_ARG;
+  if (is_share(plan)) return ROUTE_E_SHAPE;
   if (int st = check_rows(plan, rows)) return st;
   if (misaligned(logits) || misaligned(ids) || misaligned(weights) || misaligned(workspace))
     return ROUTE_E_ALIGN;
@@ -165,7 +180,9 @@ const char* route_strerror(int status) {
     case ROUTE_OK: return "ok";
     case ROUTE_E_ARG: return "invalid argument (NULL pointer, ABI version or mode)";
     case ROUTE_E_ROWS: return "row count outside the prepared envelope";
-    case ROUTE_E_SHAPE: return "shape differs from hidden 7168 / latent 3584 / experts 896 / top-16";
+    case ROUTE_E_SHAPE:
+      return "shape is not hidden 7168 / top-16 with latent x experts 3584 x 896 (or, decode only, "
+             "a rank share 448 x 112 or 224 x 56), or the call needs the whole route";
     case ROUTE_E_ALIGN: return "device pointer not 16-byte aligned";
     case ROUTE_E_DEVICE: return "device missing, not gfx950, or not the current device";
     case ROUTE_E_HIP: return "HIP launch failed";

@@ -14,14 +14,17 @@ struct DecodeWorkspace {
   double* rt_part;     // [kSplits][rows_cap][896]
 };
 
-size_t decode_workspace_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits,
-                              size_t* off_cand);
+// Decode output shapes: the whole route (3584, 896) or one tensor-parallel
+// rank's share of it, (448, 112) at 8 ranks and (224, 56) at 16 ranks.
+bool decode_shape_valid(int latent, int experts);
+size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off_lat, size_t* off_rt,
+                              size_t* off_logits, size_t* off_cand);
 size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand);
 
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
-                               const DecodeWorkspace& ws, int rows, int rows_cap, bool fuse_topk,
-                               hipStream_t stream);
+                               const DecodeWorkspace& ws, int rows, int rows_cap, int n_latent,
+                               int n_experts, bool fuse_topk, hipStream_t stream);
 
 hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,
                          hipStream_t stream);

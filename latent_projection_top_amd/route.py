@@ -20,6 +20,9 @@ EXPERTS = 896
 TOPK = 16
 DECODE_MAX_ROWS = 20
 PREFILL_MAX_ROWS = 3072
+# Decode plans may also cover one tensor-parallel rank's share of the route:
+# ranks -> (latent columns, experts) of the share.
+RANK_SHARES = {8: (448, 112), 16: (224, 56)}
 ABI_VERSION = 1
 MODE_DECODE = 0
 MODE_PREFILL = 1
@@ -98,16 +101,19 @@ def prepare_raw(cfg) -> tuple[int, int]:
 class Plan:
     """A prepared route plan (owns the C plan; freed on close/GC)."""
 
-    def __init__(self, mode: int, rows: int, device: int | None = None):
+    def __init__(self, mode: int, rows: int, device: int | None = None, latent: int = LATENT,
+                 experts: int = EXPERTS):
         if device is None:
             device = torch.cuda.current_device()
-        st, handle = prepare_raw(make_config(mode, rows, device))
+        st, handle = prepare_raw(make_config(mode, rows, device, latent=latent, experts=experts))
         if st != OK:
             raise RouteError(st, "route_prepare")
         self.handle = handle
         self.mode = mode
         self.rows = rows
         self.device = device
+        self.latent = latent
+        self.experts = experts
         self.workspace_bytes = int(LIB.route_workspace_bytes(ctypes.c_void_p(handle)))
 
     def new_workspace(self) -> torch.Tensor:
@@ -152,10 +158,10 @@ def latent_router(plan: Plan, x, w_latent, w_router, latent, logits, workspace,
     st = LIB.route_latent_router(
         ctypes.c_void_p(plan.handle),
         _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
-        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent"),
-        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router"),
-        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
-        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, plan.latent), "w_latent"),
+        _ptr(w_router, torch.float32, (HIDDEN, plan.experts), "w_router"),
+        _ptr(latent, torch.bfloat16, (rows, plan.latent), "latent"),
+        _ptr(logits, torch.float32, (rows, plan.experts), "logits"),
         _ptr(workspace, torch.uint8, None, "workspace"),
         int(rows), _stream(stream))
     if st != OK:

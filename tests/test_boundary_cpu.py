@@ -82,6 +82,11 @@ def test_prepare_null_arguments():
     ({"hidden": 7169}, route.E_SHAPE),
     ({"latent": 448}, route.E_SHAPE),
     ({"experts": 56}, route.E_SHAPE),
+    ({"latent": 448, "experts": 56}, route.E_SHAPE),
+    ({"latent": 224, "experts": 112}, route.E_SHAPE),
+    ({"latent": 896, "experts": 224}, route.E_SHAPE),
+    ({"mode": route.MODE_PREFILL, "latent": 448, "experts": 112}, route.E_SHAPE),
+    ({"mode": route.MODE_PREFILL, "latent": 224, "experts": 56}, route.E_SHAPE),
     ({"topk": 8}, route.E_SHAPE),
     ({"rows": 0}, route.E_ROWS),
     ({"rows": -3}, route.E_ROWS),
@@ -121,6 +126,40 @@ def test_decode_envelope_matches_page():
         else:
             assert st == route.E_DEVICE and handle == 0
     assert _prep(rows=f["rejected"])[0] == route.E_ROWS
+
+
+def _have_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def test_rank_shares_match_pages():
+    """The decode share shapes are the per-rank outputs the pages print: 448
+    latent columns per rank at 8 ranks, [8, 224] BF16 latent and [8, 56] FP32
+    router per rank at 16 ranks."""
+    f = FACTS["router_fp32_per_rank_tp16"]
+    assert route.RANK_SHARES[16] == (f["latent_cols"], f["cols"])
+    assert route.RANK_SHARES[8][0] == FACTS["latent_columns_per_rank_tp8"]["value"]
+    for ranks, (lat, exp) in route.RANK_SHARES.items():
+        assert lat * ranks == route.LATENT and exp * ranks == route.EXPERTS
+
+
+@pytest.mark.parametrize("ranks", sorted(route.RANK_SHARES))
+def test_rank_share_passes_validation(ranks):
+    """A decode share (1..20 rows) passes every argument check; without a GPU
+    it stops at the device check."""
+    lat, exp = route.RANK_SHARES[ranks]
+    for rows in (1, 8, 20):
+        st, handle = _prep(rows=rows, latent=lat, experts=exp)
+        if _have_gpu():
+            assert st == route.OK
+            route.LIB.route_destroy(ctypes.c_void_p(handle))
+        else:
+            assert st == route.E_DEVICE and handle == 0
+    assert _prep(rows=21, latent=lat, experts=exp)[0] == route.E_ROWS
 
 
 def test_run_calls_reject_null_plan():
