@@ -196,17 +196,24 @@ __device__ __forceinline__ void hidden_rows(const DecodeArgs& a, int m, int (&xr
   for (int nt = 0; nt < NT; ++nt) xr[nt] = min(16 * nt + m, a.rows - 1);
 }
 
+// Router rows 16..19 (17..20-row calls) on the FP64 VALU instead of a second
+// 16-row MFMA block: the MFMA would pad 4 rows to 16, and FP64 MFMA and VALU
+// have the same peak on this chip, so the VALU does the 4 rows at a quarter of
+// the cost. Their hidden values for the unit's K chunk are staged in LDS.
+constexpr int kTailRows = kDecodeMaxRows - 16;
+
 // Returns true in the workgroup that combined the last router tile: every
 // logit of every row is then stored.
 template <int NT, class Sh>
 __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
+  constexpr bool kTail = NT == 2;                     // rows 16..19 on the VALU
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int m = lane & 15;
   constexpr int kRowsPad = rows_kept<NT>();
-  int xr[NT];
-  hidden_rows<NT>(a, m, xr);
+  int xr[1];
+  hidden_rows<1>(a, m, xr);
 
   const int tile = u % Sh::RtTiles;
   const int split = u / Sh::RtTiles;
@@ -216,57 +223,101 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   const int ecol = Sh::E % kRtTileE == 0 ? e0 + 2 * m : min(e0 + 2 * m, Sh::E - 2);
   const float* wp = a.wr + (size_t)(k0 + 4 * g) * Sh::E + ecol;
 
-  f64x4 acc[NT][2];
+  // LDS after the reduction buffer: hidden rows 16..19 over the unit's K chunk
+  uint16_t* xt = reinterpret_cast<uint16_t*>(smem + kWaves * kRowsPad * kRtTileE * 8);
+  constexpr int kTailChunks = kTailRows * Sh::KR / 8;  // 16-byte pieces
+  static_assert(!kTail || kTailChunks <= kThreads, "one piece per thread");
+  u32x4 xtv = u32x4{0u, 0u, 0u, 0u};
+  if (kTail && (int)threadIdx.x < kTailChunks) {
+    const int i = threadIdx.x / (Sh::KR / 8);
+    const int c = threadIdx.x % (Sh::KR / 8);
+    xtv = *(const u32x4*)(a.x + (size_t)min(16 + i, a.rows - 1) * kHidden + split * Sh::KR + 8 * c);
+  }
+
+  f64x4 acc[2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int c = 0; c < 2; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+  double tacc[kTailRows][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc[nt][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-  constexpr int kDepthR = Sh::StepsR < 4 ? Sh::StepsR : 4;
+  for (int i = 0; i < kTailRows; ++i) tacc[i][0] = tacc[i][1] = 0.0;
+  constexpr int kDepthR = Sh::StepsR;
+  static_assert(kDepthR <= 8, "router prefetch ring fits the register budget");
   f32x2 wv[kDepthR][4];
-  u32x2 xv[kDepthR][NT];
+  u32x2 xv[kDepthR];
   auto issue = [&](int st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       wv[st % kDepthR][j] =
           __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStepR + j) * Sh::E));
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      xv[st % kDepthR][nt] = *(const u32x2*)(a.x + (size_t)xr[nt] * kHidden + k0 + 4 * g + st * kStepR);
+    xv[st % kDepthR] = *(const u32x2*)(a.x + (size_t)xr[0] * kHidden + k0 + 4 * g + st * kStepR);
   };
+  // every step's loads are issued up front (measured: 0.3 us faster at 8 rows
+  // and 0.5 us at 20 rows than 4 steps ahead, at the same register count)
 #pragma unroll
   for (int st = 0; st < kDepthR; ++st) issue(st);
   __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
+  if (kTail) {
+    if ((int)threadIdx.x < kTailChunks) {
+      const int i = threadIdx.x / (Sh::KR / 8);
+      const int c = threadIdx.x % (Sh::KR / 8);
+      *(u32x4*)(xt + i * Sh::KR + 8 * c) = xtv;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int st = 0; st < Sh::StepsR; ++st) {
     const int q = st % kDepthR;
     // lane (g, m) at step j: A[m][g] = Wr[k][e0 + 2m + c], B[g][m] = x[row m][k],
     // k = k0 + 16*st + 4*g + j
+    u32x2 xtl[kTailRows];
+    if (kTail) {
+#pragma unroll
+      for (int i = 0; i < kTailRows; ++i)
+        xtl[i] = *(const u32x2*)(xt + i * Sh::KR + wave * Sh::KRWave + st * kStepR + 4 * g);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const double w0 = (double)wv[q][j][0];
       const double w1 = (double)wv[q][j][1];
+      const double xd = (double)((j & 1) ? bf16_hi(xv[q][j >> 1]) : bf16_lo(xv[q][j >> 1]));
+      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(w0, xd, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w1, xd, acc[1], 0, 0, 0);
+      if (kTail) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const double xd = (double)((j & 1) ? bf16_hi(xv[q][nt][j >> 1]) : bf16_lo(xv[q][nt][j >> 1]));
-        acc[nt][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(w0, xd, acc[nt][0], 0, 0, 0);
-        acc[nt][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w1, xd, acc[nt][1], 0, 0, 0);
+        for (int i = 0; i < kTailRows; ++i) {
+          const double xi = (double)((j & 1) ? bf16_hi(xtl[i][j >> 1]) : bf16_lo(xtl[i][j >> 1]));
+          tacc[i][0] = fma(w0, xi, tacc[i][0]);
+          tacc[i][1] = fma(w1, xi, tacc[i][1]);
+        }
       }
     }
-    if (st + kDepthR < Sh::StepsR) issue(st + kDepthR);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kTail) {
+    // lane (g, m) summed K rows 4g..4g+3 of each step: add the four g groups
+#pragma unroll
+    for (int i = 0; i < kTailRows; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        tacc[i][c] += __shfl_xor(tacc[i][c], 16);
+        tacc[i][c] += __shfl_xor(tacc[i][c], 32);
+      }
   }
 
   double* red = reinterpret_cast<double*>(smem);
   // The FP64 MFMA keeps D[4*t + g][m] in slot t of lane (g, m): lane (g, m)
-  // holds row 16*nt + m, local experts 2*(4*t + g) + c = 8*t + 2*g + c.
+  // holds row m, local experts 2*(4*t + g) + c = 8*t + 2*g + c.
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int t = 0; t < 4; ++t)
+      red[(wave * kRowsPad + m) * kRtTileE + 8 * t + 2 * g + c] = acc[c][t];
+  if (kTail && g == 0) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (16 * nt + m < kRowsPad)
-          red[(wave * kRowsPad + 16 * nt + m) * kRtTileE + 8 * t + 2 * g + c] = acc[nt][c][t];
+    for (int i = 0; i < kTailRows; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) red[(wave * kRowsPad + 16 + i) * kRtTileE + 2 * m + c] = tacc[i][c];
+  }
   __syncthreads();
   const int outs = a.rows * kRtTileE;
   for (int i = threadIdx.x; i < outs; i += kThreads) {
@@ -466,7 +517,8 @@ template <int NT, class Sh>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_route_kernel(DecodeArgs a) {
   constexpr int kLatBytes = kWaves * rows_kept<NT>() * kLatTileN * 4;
-  constexpr int kRtBytes = kWaves * rows_kept<NT>() * kRtTileE * 8;
+  constexpr int kRtBytes = kWaves * rows_kept<NT>() * kRtTileE * 8 +
+                           (NT == 2 ? kTailRows * Sh::KR * 2 : 0);   // + staged hidden rows
   constexpr int kRowBytes = kRowGroup * kTopkScratch * 8;
   constexpr int kB0 = kLatBytes > kRtBytes ? kLatBytes : kRtBytes;
   constexpr int kBytes = kB0 > kRowBytes ? kB0 : kRowBytes;
