@@ -33,8 +33,10 @@
  *     synchronises; run calls only enqueue kernels on `stream`, so they can be
  *     captured into a HIP graph;
  *   - the workspace (route_workspace_bytes) must be zero-filled once by the
- *     caller before its first use; every call leaves its counters at zero
- *     again. Two calls that overlap in time must use different workspaces;
+ *     caller before its first use; decode calls keep a few counters in it
+ *     from one call to the next, so it must not be modified between calls
+ *     (zero-filling it again is allowed). Two calls that overlap in time must
+ *     use different workspaces;
  *   - a plan is immutable after route_prepare and may be shared by threads.
  *
  * Layouts (row-major, all device pointers, 16-byte aligned):

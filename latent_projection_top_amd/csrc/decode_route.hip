@@ -13,7 +13,9 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split: 672 workgroups of 4 waves, all resident at once.
+// Work split (whole route; a tensor-parallel rank's share uses the same units
+// over its columns with more K splits): 672 workgroups of 4 waves, all
+// resident at once.
 //   workgroups 0..447, dispatched first: router units, expert tile (32
 //       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
 //       bytes) of the FP32 router weight and the unit stores one FP64 partial
@@ -24,8 +26,9 @@
 // Router waves have a quarter of a latent wave's bytes and finish early; the
 // workgroup that combines the last router tile then selects the top-16 of
 // every row, four rows at a time (one per wave), while the latent weight is
-// still streaming, and latent workgroups take any rows left when they finish. Nothing ever waits for another workgroup; every unit's arithmetic
-// and combine order is fixed, so results do not depend on scheduling.
+// still streaming, and latent workgroups take any rows left when they finish.
+// Nothing ever waits for another workgroup; every unit's arithmetic and
+// combine order is fixed, so results do not depend on scheduling.
 //
 // Latent unit, per wave and 32-row step: each lane reads 8 rows x 4 columns
 // (8-byte loads; 16 lanes cover one 128-byte row segment), transposes the 8x4
@@ -36,8 +39,9 @@
 // FP64; the last unit of a tile sums the 4 partials in FP64 and rounds once.
 //
 // Router unit, per wave and 16-row step: v_mfma_f64_16x16x4_f64 with the FP32
-// weights and the BF16 hidden values widened exactly to FP64, so the logits
-// are accumulated in FP64 end to end and rounded to FP32 once.
+// weights and the BF16 hidden values widened exactly to FP64 (rows 16..19 as
+// FP64 FMAs on the VALU), so the logits are accumulated in FP64 end to end and
+// rounded to FP32 once.
 #include "route_device.h"
 #include "route_launch.h"
 
@@ -84,13 +88,11 @@ struct DecodeShape {
   // Workspace counters (uint32). Every counter is shared by few workgroups:
   // atomics on one address from hundreds of workgroups serialise.
   static constexpr int CtrRtTile = LatTiles;          // router units stored per tile
-  static constexpr int CtrRouter = LatTiles + RtTiles;  // router tiles combined
-  static constexpr int CtrRows = CtrRouter + 1;       // rows claimed
-  static constexpr int CtrFin = CtrRouter + 2;        // row-phase participants finished
-  static constexpr int Counters = CtrRouter + 3;
-  // Row-phase participants: the workgroup that combines the last router tile
-  // and the workgroups that combine a latent tile, each once per call.
-  static constexpr int RowParticipants = 1 + LatTiles;
+  static constexpr int CtrPar = LatTiles + RtTiles;   // parity of the call (whole route)
+  // two 8-byte-aligned pairs {router tiles combined, row groups claimed}, one
+  // per call parity
+  static constexpr int CtrPair = (CtrPar + 2) & ~1;
+  static constexpr int Counters = CtrPair + 4;
   static_assert(KL * SplitsL == kHidden && KR * SplitsR == kHidden, "the splits cover K");
   static_assert(KLWave % kStepL == 0 && KRWave % kStepR == 0, "whole steps per wave");
   static_assert(N % 4 == 0 && E % 2 == 0, "a lane's loads stay inside a row");
@@ -205,7 +207,7 @@ constexpr int kTailRows = kDecodeMaxRows - 16;
 // Returns true in the workgroup that combined the last router tile: every
 // logit of every row is then stored.
 template <int NT, class Sh>
-__device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
+__device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* slot, uint32_t* pair) {
   constexpr bool kTail = NT == 2;                     // rows 16..19 on the VALU
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -360,7 +362,7 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
     }
   }
   if (threadIdx.x == 0) st_dev(&a.counters[Sh::CtrRtTile + tile], 0u);
-  return publish(&a.counters[Sh::CtrRouter], slot) == (uint32_t)(Sh::RtTiles - 1);
+  return publish(&pair[0], slot) == (uint32_t)(Sh::RtTiles - 1);
 }
 
 template <int NT, class Sh>
@@ -479,7 +481,6 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
 // the fused call wave w selects the top-16 of row r0 + w, reading the logits
 // with coherent loads (other workgroups of this launch wrote them).
 __device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
-  if (!a.fuse_topk) return;
   uint64_t* scratch = reinterpret_cast<uint64_t*>(smem);
   const int nr = min(kRowGroup, a.rows - r0);
   const int w = threadIdx.x >> 6;
@@ -489,17 +490,23 @@ __device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
   __syncthreads();
 }
 
-// Claim the next group of rows if every router tile has been combined.
-// Group 0 (rows 0..3) belongs to the workgroup that completed the router,
-// which starts on it without a claim; the counter hands out the later groups.
-// Returns the group's first row, or -1 when the router phase is not complete
-// or no row is left. `router_done` is thread 0's knowledge that it is complete.
+// Claim the next group of rows. Group 0 (rows 0..3) belongs to the workgroup
+// that completed the router, which starts on it without a claim; pair[1]
+// hands out the later groups. A latent workgroup first reads the pair in one
+// coherent load and claims only if the router is complete and a group is
+// left. Returns the group's first row, or -1. Thread 0 holds `pair`.
 template <class Sh>
-__device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done, int* slot) {
+__device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done, uint32_t* pair,
+                                          int* slot) {
   int r = -1;
   if (threadIdx.x == 0) {
-    if (router_done || ld_dev(&a.counters[Sh::CtrRouter]) == (uint32_t)Sh::RtTiles) {
-      const uint32_t c = kRowGroup + add_dev(&a.counters[Sh::CtrRows], (uint32_t)kRowGroup);
+    bool go = router_done;
+    if (!go) {
+      const uint64_t v = ld_dev(reinterpret_cast<const uint64_t*>(pair));
+      go = (uint32_t)v == (uint32_t)Sh::RtTiles && kRowGroup + (uint32_t)(v >> 32) < (uint32_t)a.rows;
+    }
+    if (go) {
+      const uint32_t c = kRowGroup + add_dev(&pair[1], (uint32_t)kRowGroup);
       if (c < (uint32_t)a.rows) r = (int)c;
     }
   }
@@ -507,12 +514,20 @@ __device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done,
 }
 
 // Workgroup b < Sh::RtUnits (448 for the whole route) runs router unit b, the
-// others latent unit b - Sh::RtUnits. Row groups (the fused top-16) are taken
-// by the workgroup that combines the last router tile, until none is left, and
-// by every workgroup that combines a latent tile, if the logits are complete by
-// then. These participants (57 for the whole route) each bump CtrFin once when
-// they stop taking rows; the last resets the row-phase counters for the next
-// call.
+// others latent unit b - Sh::RtUnits.
+//
+// Row phase (the fused top-16 of the whole route). Row groups are taken by
+// the workgroup that combines the last router tile, until none is left, and
+// by any workgroup that combines a latent tile after the logits are complete.
+// Nobody waits and nobody counts the participants out: the two counters of
+// the phase live in one of two pairs chosen by the call's parity, which
+// thread 0 of every workgroup reads at its start. The workgroup that
+// completed the router, after its last group, clears the other pair (last
+// used by the previous call, which has ended) and flips the parity for the
+// next call. Every router unit reads the parity before its tile can be
+// combined, so every increment of this call's router counter lands in this
+// call's pair; a latent workgroup that read the flipped parity would only
+// find a cleared pair and take no row.
 template <int NT, class Sh>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_route_kernel(DecodeArgs a) {
@@ -526,9 +541,12 @@ void decode_route_kernel(DecodeArgs a) {
   __shared__ int slot;
 
   const int b = blockIdx.x;
+  uint32_t par = 0;
+  if (Sh::kFull && threadIdx.x == 0) par = ld_dev(&a.counters[Sh::CtrPar]) & 1u;
+  uint32_t* pair = &a.counters[Sh::CtrPair + 2 * par];
   bool router_done = false;
   if (b < Sh::RtUnits) {
-    router_done = router_unit<NT, Sh>(a, b, smem, &slot);
+    router_done = router_unit<NT, Sh>(a, b, smem, &slot, pair);
     if (!router_done) return;
   } else if (!latent_unit<NT, Sh>(a, b - Sh::RtUnits, smem, &slot)) {
     return;
@@ -536,17 +554,22 @@ void decode_route_kernel(DecodeArgs a) {
   if constexpr (!Sh::kFull) {
     // A share has no row phase (its experts are a fraction of the route's, so
     // there is nothing to select): the workgroup that combined the last router
-    // tile resets the router counter, and the call ends.
-    if (router_done && threadIdx.x == 0) st_dev(&a.counters[Sh::CtrRouter], 0u);
+    // tile clears the router counter, and the call ends.
+    if (router_done && threadIdx.x == 0) st_dev(&pair[0], 0u);
     return;
   }
-  if (router_done) row_group(a, 0, smem);
-  for (int r = claim_rows<Sh>(a, router_done, &slot); r >= 0; r = claim_rows<Sh>(a, router_done, &slot))
+  int r = !a.fuse_topk ? -1 : router_done ? 0 : claim_rows<Sh>(a, false, pair, &slot);
+  while (r >= 0) {
     row_group(a, r, smem);
-  if (publish(&a.counters[Sh::CtrFin], &slot) == (uint32_t)(Sh::RowParticipants - 1) && threadIdx.x == 0) {
-    st_dev(&a.counters[Sh::CtrRouter], 0u);
-    st_dev(&a.counters[Sh::CtrRows], 0u);
-    st_dev(&a.counters[Sh::CtrFin], 0u);
+    // groups are handed out in order: none is left after the one that ends
+    // at or past the last row (and the router is known complete by now)
+    r = r + kRowGroup < a.rows ? claim_rows<Sh>(a, true, pair, &slot) : -1;
+  }
+  if (router_done && threadIdx.x == 0) {
+    uint32_t* other = &a.counters[Sh::CtrPair + 2 * (par ^ 1u)];
+    st_dev(&other[0], 0u);
+    st_dev(&other[1], 0u);
+    st_dev(&a.counters[Sh::CtrPar], par ^ 1u);
   }
 }
 

@@ -87,3 +87,13 @@ class Outputs:
             "ids": self.ids[r].cpu().numpy(),
             "weights": self.weights[r].cpu().numpy(),
         }
+
+
+def decode_counters_idle(ws: torch.Tensor) -> bool:
+    """State a whole-route decode workspace is left in after every call: the
+    84 per-tile counters at zero, the row-phase parity 0 or 1, and the
+    counter pair the next call will use cleared."""
+    c = ws[:512].view(torch.int32).cpu().numpy()
+    par = int(c[84])
+    return bool((c[:84] == 0).all() and par in (0, 1) and c[85] == 0
+                and c[86 + 2 * par] == 0 and c[87 + 2 * par] == 0 and (c[90:] == 0).all())

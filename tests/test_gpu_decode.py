@@ -14,7 +14,8 @@ import torch
 from oracle import compare
 from oracle import route_oracle as orc
 from synth import generators as gen
-from tests.routekit import Outputs, bf16_dev, bits_host, log, oracle_rows, weights_dev
+from tests.routekit import (Outputs, bf16_dev, bits_host, decode_counters_idle, log, oracle_rows,
+                            weights_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,8 +71,8 @@ def test_decode_banks(width):
     log(f"decode parity width={width} banks={BANKS}")
     xs, got, ws = run_banks(width, BANKS, fused=(width % 2 == 0))
     judge(xs, got, f"decode w={width}")
-    # every counter the kernels used (the first 256 bytes) is back at zero
-    assert int(ws[:256].count_nonzero()) == 0
+    # the tile counters are back at zero and the next call's pair is cleared
+    assert decode_counters_idle(ws)
 
 
 @pytest.mark.parametrize("width", list(range(1, 21)))
@@ -94,11 +95,20 @@ def test_rows_below_plan_capacity_and_repeat_determinism():
     xs = gen.hidden(20, bank=77)
     xd = bf16_dev(xs)
     outs = []
-    for rows in (20, 5, 20, 13, 1, 20):
+    for i, rows in enumerate((20, 5, 20, 13, 1, 20, 7, 20)):
         o = Outputs(20)
         o.poison()
+        if i == 4:
+            # a projection-only call on the same workspace, then the
+            # workspace zero-filled again: both leave it usable
+            route.latent_router(plan, xd, w, wr, o.latent, o.logits, ws, rows=20)
+            torch.cuda.synchronize()
+            assert decode_counters_idle(ws)
+            ws.zero_()
+            o.poison()
         route.fused(plan, xd, w, wr, o.latent, o.logits, o.ids, o.weights, ws, rows=rows)
         torch.cuda.synchronize()
+        assert decode_counters_idle(ws)
         h = o.host()
         outs.append((rows, h))
         # rows beyond `rows` are untouched
