@@ -179,61 +179,114 @@ __device__ __forceinline__ uint64_t select16_rounds(const uint64_t (&keys)[P]) {
   return mine;
 }
 
-// LDS (uint64 slots) one wave of select16 needs: 64 lane maxima, 64
-// candidates + 8 zero pads, 16 selected.
-constexpr int kTopkScratch = 64 + 72 + kTopK;
+// LDS (uint64 slots) one wave of select16 needs: 64 candidates + 8 zero pads,
+// 16 selected, and a slot that takes the stores of lanes with no candidate
+// (one more keeps each wave's area a multiple of 16 bytes).
+constexpr int kTopkScratch = 72 + kTopK + 2;
+constexpr int kTopkDiscard = 72 + kTopK;
+constexpr int kRankBatch = 24;   // candidates every lane reads in one batch
+
+// Population count of a wave-wide ballot (two 32-bit counts, so that the
+// compare that follows stays a scalar instruction).
+__device__ __forceinline__ uint32_t mask_count(uint64_t m) {
+  return (uint32_t)__builtin_popcount((uint32_t)m) + (uint32_t)__builtin_popcount((uint32_t)(m >> 32));
+}
+__device__ __forceinline__ uint32_t ballot_count(bool p) { return mask_count(ballot(p)); }
+
+// The largest t with at least `need` lanes holding v >= t among the lanes
+// where `in` is true, i.e. the need-th largest v of those lanes, built bit by
+// bit from the top (ballots and scalar counts only, no memory; measured
+// faster than two bits per step with three ballots).
+__device__ __forceinline__ uint32_t nth_largest_u32(uint32_t v, bool in, uint32_t need) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if (ballot_count(in && v >= c) >= need) t = c;
+  }
+  return t;
+}
 
 // One wave selects the 16 largest of a set of distinct 64-bit keys, P per
 // lane (a zero key is padding: it is below every real key). At least 16
 // lanes must hold a real key. Returns, in lane s < 16, the s-th largest key.
-//   1. Threshold: t0 = the 16th largest of the 64 lane maxima; every lane
-//      ranks its maximum against all 64 through LDS. At least 16 keys are
-//      >= t0, so the top 16 are among them.
+//   1. Threshold: t0 = the 16th largest of the 64 lane maxima, found with a
+//      bitwise search on the logit half (32 ballots) and, only when several
+//      lane maxima share that logit, on the index half among them. At least
+//      16 keys are >= t0, so the top 16 are among them.
 //   2. The keys >= t0 (typically about 20) are compacted into LDS in ballot
 //      order; each ranks itself against all of them, and rank r < 16 is the
 //      r-th selected key.
 //   3. More than 64 keys >= t0 take the sort-and-rounds fallback, which
 //      selects the same keys.
+// Every step is written so that its LDS accesses and ballots are independent
+// and can be in flight together: one wave runs this alone, so latency, not
+// throughput, sets its time.
 // scratch: kTopkScratch uint64 slots of LDS owned by this wave. Waves are
 // independent (no workgroup barrier inside).
 template <int P>
 __device__ __forceinline__ uint64_t select16(const uint64_t (&c)[P], uint64_t* scratch) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint64_t mx = c[0];
+  // lane maximum, pairwise
+  uint64_t m[P];
 #pragma unroll
-  for (int i = 1; i < P; ++i) mx = c[i] > mx ? c[i] : mx;
+  for (int i = 0; i < P; ++i) m[i] = c[i];
+#pragma unroll
+  for (int w = 1; w < P; w *= 2)
+#pragma unroll
+    for (int i = 0; i + w < P; i += 2 * w) m[i] = m[i + w] > m[i] ? m[i + w] : m[i];
+  const uint64_t mx = m[0];
 
-  uint64_t* lmax = scratch;
-  uint64_t* cand = scratch + 64;
-  uint64_t* sel = scratch + 64 + 72;
-  // (one wave's LDS accesses are performed in order: a read after a write
-  // sees it without a barrier)
-  lmax[lane] = mx;
-  uint32_t rk = 0;
-#pragma unroll
-  for (int j = 0; j < kWave; j += 2) {
-    const u64x2 v = *reinterpret_cast<const u64x2*>(lmax + j);
-    rk += (v[0] > mx ? 1u : 0u) + (v[1] > mx ? 1u : 0u);
+  // 1. the real lane maxima are distinct and at least 16 of them are above
+  //    every padding lane, so the 16th largest is one lane's maximum
+  const uint32_t hi = (uint32_t)(mx >> 32);
+  const uint32_t th = nth_largest_u32(hi, true, kTopK);
+  const uint64_t eq = ballot(hi == th);
+  uint64_t t0;
+  if (mask_count(eq) == 1u) {
+    t0 = readlane_u64(mx, __builtin_ctzll(eq));
+  } else {
+    const uint32_t need = kTopK - ballot_count(hi > th);
+    t0 = ((uint64_t)th << 32) | nth_largest_u32((uint32_t)mx, hi == th, need);
   }
-  // the real lane maxima are distinct and at least 16 of them rank above
-  // every padding lane, so exactly one lane has rank 15
-  const uint64_t t0 = readlane_u64(mx, __builtin_ctzll(ballot(rk == 15u)));
 
-  uint32_t n = 0;  // keys >= t0 so far (wave-uniform)
+  // 2. compaction: every ballot first, then the scalar prefix counts, then
+  //    the stores
+  uint64_t* cand = scratch;
+  uint64_t* sel = scratch + 72;
+  uint64_t msk[P];
+  uint32_t base[P];
+  uint32_t n = 0;  // keys >= t0 (wave-uniform)
+#pragma unroll
+  for (int i = 0; i < P; ++i) msk[i] = ballot(c[i] >= t0);
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    const bool p = c[i] >= t0;
-    const uint64_t msk = ballot(p);
-    const uint32_t pos = n + lanes_below(msk);
-    if (p && pos < (uint32_t)kWave) cand[pos] = c[i];
-    n += (uint32_t)__builtin_popcountll(msk);
+    base[i] = n;
+    n += mask_count(msk[i]);
   }
   if (n > (uint32_t)kWave) return select16_rounds<P>(c);
-  // zero pads up to a multiple of 8
-  if (lane < 8) cand[n + lane] = 0ull;
+  // (a lane without a candidate stores to the discard slot: no branches)
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    cand[c[i] >= t0 ? base[i] + lanes_below(msk[i]) : (uint32_t)kTopkDiscard] = c[i];
+  // zero pads: up to the first batch, and up to a multiple of 8 beyond it
+  if ((uint32_t)lane >= n && lane < kRankBatch) cand[lane] = 0ull;
+  if (n > (uint32_t)kRankBatch && lane < 8) cand[n + lane] = 0ull;
+
+  // 3. rank: the first 24 candidates in one batch of loads, the rest (rare)
+  //    8 at a time
   const uint64_t mine = (uint32_t)lane < n ? cand[lane] : 0ull;
+  uint64_t v[kRankBatch];
+#pragma unroll
+  for (int j = 0; j < kRankBatch; j += 2) {
+    const u64x2 q = *reinterpret_cast<const u64x2*>(cand + j);
+    v[j] = q[0];
+    v[j + 1] = q[1];
+  }
   uint32_t r = 0;
-  for (uint32_t j = 0; j < n; j += 8) {
+#pragma unroll
+  for (int j = 0; j < kRankBatch; ++j) r += v[j] > mine ? 1u : 0u;
+  for (uint32_t j = kRankBatch; j < n; j += 8) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) r += cand[j + q] > mine ? 1u : 0u;
   }
@@ -241,9 +294,29 @@ __device__ __forceinline__ uint64_t select16(const uint64_t (&c)[P], uint64_t* s
   return lane < kTopK ? sel[lane] : 0ull;
 }
 
+// Sum over lanes 0..15 of an FP64 value (0 in lanes 16..63), the same in every
+// lane: an inclusive scan within the first 16-lane row (shifts by 1, 2, 4, 8;
+// a lane without a source adds 0) leaves the total in lane 15, which is then
+// broadcast. The order of the additions is fixed.
+template <int Ctrl>
+__device__ __forceinline__ double dpp_shr_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, Ctrl, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), Ctrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double sum16_f64(double v) {
+  v += dpp_shr_f64<kRowShr1>(v);
+  v += dpp_shr_f64<kRowShr2>(v);
+  v += dpp_shr_f64<kRowShr4>(v);
+  v += dpp_shr_f64<kRowShr8>(v);
+  return __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(v), 15));
+}
+
 // Lanes s < 16 hold the s-th selected key: write the ids (selection order)
 // and the weights, sigmoid in FP64 of the selected logit (recovered from its
-// key) normalised over the 16 in a fixed tree, rounded once to FP32.
+// key) normalised over the 16 in a fixed order, rounded once to FP32.
 __device__ __forceinline__ void write_selection(uint64_t k, int32_t* __restrict__ ids,
                                                 float* __restrict__ weights) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -253,9 +326,7 @@ __device__ __forceinline__ void write_selection(uint64_t k, int32_t* __restrict_
     const double v = (double)key_logit((uint32_t)(k >> 32));
     s = 1.0 / (1.0 + exp(-v));
   }
-  double tot = s;
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 16);
+  const double tot = sum16_f64(s);
   if (lane < kTopK) {
     ids[lane] = (int32_t)my_idx;
     weights[lane] = (float)(s / tot);
