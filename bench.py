@@ -309,7 +309,7 @@ def main():
         w0, wr0 = copies[0]
 
         def t_call(fn, reps):
-            for _ in range(3):
+            for _ in range(10):
                 fn()
             torch.cuda.synchronize()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -320,9 +320,10 @@ def main():
             torch.cuda.synchronize()
             return s.elapsed_time(e) / reps * 1000.0
 
+        # the whole chunk first (it is the reported figure), then its pieces
+        t_all = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
         t_tk = t_call(lambda: route.topk16(plan, lg, ids, wt), args.prefill_reps)
-        t_all = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
         gemm_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER_MFMA
         prefill = {
             "rows": rows, "us_per_chunk": round(t_all, 2), "rows_per_s": round(rows / (t_all * 1e-6)),
