@@ -114,3 +114,93 @@ def test_cancelling_partials_single_rounding():
         assert lc["fail"] == 0
         assert lc["rel_rms"] <= 2.0e-3
         assert lc["rel_rms"] <= 0.1 * rr_two
+
+
+@pytest.mark.timeout(300)
+def test_concurrent_streams_with_distinct_workspaces():
+    """Calls that overlap in time are allowed when each has its own workspace:
+    two streams run decode routes (8 and 20 rows, one plan each) and a prefill
+    chunk concurrently, 40 rounds, and every output equals the same call run
+    alone."""
+    log("concurrent decode/decode/prefill on three streams, distinct workspaces")
+    w, wr = weights_dev(0)
+    cases = [(route.MODE_DECODE, 8), (route.MODE_DECODE, 20), (route.MODE_PREFILL, 96)]
+    setups = []
+    for k, (mode, rows) in enumerate(cases):
+        plan = route.Plan(mode, rows)
+        xs = [bf16_dev(gen.hidden(rows, bank=30000 + 100 * k + b)) for b in range(4)]
+        setups.append((plan, plan.new_workspace(), xs, rows))
+    # references: each call alone, synchronised
+    refs = []
+    for plan, ws, xs, rows in setups:
+        r = []
+        for x in xs:
+            o = Outputs(rows)
+            route.fused(plan, x, w, wr, o.latent, o.logits, o.ids, o.weights, ws)
+            torch.cuda.synchronize()
+            r.append(o.host())
+        refs.append(r)
+    streams = [torch.cuda.Stream() for _ in setups]
+    outs = [[Outputs(rows) for _ in range(40)] for (_, _, _, rows) in setups]
+    torch.cuda.synchronize()
+    for i in range(40):
+        for k, (plan, ws, xs, rows) in enumerate(setups):
+            with torch.cuda.stream(streams[k]):
+                o = outs[k][i]
+                route.fused(plan, xs[i % 4], w, wr, o.latent, o.logits, o.ids, o.weights, ws)
+    torch.cuda.synchronize()
+    for k, (plan, ws, xs, rows) in enumerate(setups):
+        for i in range(40):
+            h, r = outs[k][i].host(), refs[k][i % 4]
+            for key in ("latent", "logits", "ids"):
+                assert np.array_equal(h[key], r[key]), (k, i, key)
+            assert np.array_equal(h["weights"].view(np.uint32), r["weights"].view(np.uint32))
+        if plan.mode == route.MODE_DECODE:
+            assert decode_counters_idle(ws)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("ranks", sorted(route.RANK_SHARES))
+def test_share_graph_replay(ranks):
+    """A rank-share call captured in a HIP graph: 200 replays over rotating
+    input banks, each equal to the eager result for its bank."""
+    lat, exp = route.RANK_SHARES[ranks]
+    log(f"share graph replay ranks={ranks}")
+    wl, wrt = weights_dev(0)
+    w = wl[:, lat:2 * lat].contiguous()
+    wr = wrt[:, exp:2 * exp].contiguous()
+    plan = route.Plan(route.MODE_DECODE, 20, latent=lat, experts=exp)
+    ws = plan.new_workspace()
+    banks = [bf16_dev(gen.hidden(20, bank=31000 + b)) for b in range(8)]
+    refs = []
+    for x in banks:
+        a = torch.empty((20, lat), dtype=torch.bfloat16, device="cuda")
+        b = torch.empty((20, exp), dtype=torch.float32, device="cuda")
+        route.latent_router(plan, x, w, wr, a, b, ws)
+        refs.append((a, b))
+    torch.cuda.synchronize()
+    x_static = banks[0].clone()
+    a_out = torch.empty((20, lat), dtype=torch.bfloat16, device="cuda")
+    b_out = torch.empty((20, exp), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        route.latent_router(plan, x_static, w, wr, a_out, b_out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        a_out.view(torch.int16).fill_(-1)
+        b_out.view(torch.int32).fill_(-1)
+        route.latent_router(plan, x_static, w, wr, a_out, b_out, ws)
+    bad = 0
+    for i in range(200):
+        k = (i * 3 + 1) % 8
+        x_static.copy_(banks[k])
+        g.replay()
+        ok = torch.equal(a_out, refs[k][0]) and torch.equal(b_out.view(torch.int32),
+                                                            refs[k][1].view(torch.int32))
+        bad += 0 if ok else 1
+    torch.cuda.synchronize()
+    assert bad == 0
+    assert int(ws[:512].count_nonzero()) == 0
