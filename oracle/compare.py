@@ -1,4 +1,4 @@
-"""Comparators that judge an implementation's route outputs against the oracle.
+"""Comparators that check an implementation's route outputs against the oracle.
 
 TEST INFRASTRUCTURE (see route_oracle). Pure numpy; imports nothing from the
 HIP path.

@@ -47,7 +47,7 @@ def run_banks(width: int, banks: int, fused: bool):
     return xs, out.host(), ws
 
 
-def judge(xs, got, tag):
+def check_outputs(xs, got, tag):
     ref = oracle_rows(xs)
     lc = compare.latent_check(got["latent"], ref["latent"], ref["exact"], ref["abs_terms"])
     ld = compare.f32_ulp_distance(got["logits"], ref["logits"])
@@ -70,7 +70,7 @@ def judge(xs, got, tag):
 def test_decode_banks(width):
     log(f"decode parity width={width} banks={BANKS}")
     xs, got, ws = run_banks(width, BANKS, fused=(width % 2 == 0))
-    judge(xs, got, f"decode w={width}")
+    check_outputs(xs, got, f"decode w={width}")
     # the tile counters are back at zero and the next call's pair is cleared
     assert decode_counters_idle(ws)
 
@@ -84,7 +84,7 @@ def test_fused_equals_two_calls_bitwise(width):
         assert np.array_equal(got_a[k], got_b[k]), k
     assert np.array_equal(got_a["weights"].view(np.uint32), got_b["weights"].view(np.uint32))
     if width in (2, 3, 5, 17):
-        judge(xs_a, got_a, f"decode w={width}")
+        check_outputs(xs_a, got_a, f"decode w={width}")
 
 
 def test_rows_below_plan_capacity_and_repeat_determinism():
@@ -117,7 +117,7 @@ def test_rows_below_plan_capacity_and_repeat_determinism():
     for h in full[1:]:
         for k in ("latent", "logits", "ids"):
             assert np.array_equal(h[k], full[0][k])
-    judge(xs, full[0], "decode w=20 cap")
+    check_outputs(xs, full[0], "decode w=20 cap")
     # a row's outputs do not depend on how many rows share the call
     for rows, h in outs:
         assert np.array_equal(h["latent"][:rows], full[0]["latent"][:rows])

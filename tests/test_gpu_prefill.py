@@ -36,7 +36,7 @@ def run_prefill(x_bits, cap=3072, fused=False):
     return out.host()
 
 
-def judge(xs, got, tag):
+def check_outputs(xs, got, tag):
     ref = oracle_rows(xs)
     lc = compare.latent_check(got["latent"], ref["latent"], ref["exact"], ref["abs_terms"])
     gc = compare.logits_check(got["logits"], ref["logits"], ref["logits_exact"],
@@ -64,7 +64,7 @@ def test_prefill_chunk_3072_outliers(bank):
     log(f"prefill 3072 rows, outliers, bank={bank}")
     xs = gen.hidden(3072, bank=500 + bank, outliers=True)
     got = run_prefill(xs, fused=(bank % 2 == 1))
-    judge(xs, got, f"prefill 3072 bank {bank}")
+    check_outputs(xs, got, f"prefill 3072 bank {bank}")
 
 
 @pytest.mark.parametrize("rows", [1, 77, 130, 1000])
@@ -72,7 +72,7 @@ def test_prefill_ragged(rows):
     log(f"prefill ragged rows={rows}")
     xs = gen.hidden(rows, bank=600 + rows, outliers=True)
     got = run_prefill(xs, cap=3072)
-    judge(xs, got, f"prefill rows={rows}")
+    check_outputs(xs, got, f"prefill rows={rows}")
 
 
 def test_prefill_fused_equals_two_calls():

@@ -72,7 +72,7 @@ class ShareOutputs:
         return bits_host(self.latent), self.logits.cpu().numpy()
 
 
-def judge(xs, got_latent, got_logits, ref, tag):
+def check_outputs(xs, got_latent, got_logits, ref, tag):
     lc = compare.latent_check(got_latent, ref["latent"], ref["exact"], ref["abs_terms"])
     ld = compare.f32_ulp_distance(got_logits, ref["logits"])
     log(f"{tag}: latent {lc} | logits ulp max {ld.max()} mean {ld.mean():.3g}")
@@ -103,7 +103,7 @@ def test_share_banks(ranks, width):
         a, l_ = o.host()
         lat_h.append(a)
         lg_h.append(l_)
-    judge(xs, np.concatenate(lat_h), np.concatenate(lg_h), share_oracle(xs, ranks, rank),
+    check_outputs(xs, np.concatenate(lat_h), np.concatenate(lg_h), share_oracle(xs, ranks, rank),
           f"share {ranks} ranks w={width}")
     assert int(ws[:512].count_nonzero()) == 0
 
@@ -132,7 +132,7 @@ def test_share_rows_below_capacity_and_determinism(ranks):
     for rows, a, l_ in outs:
         assert np.array_equal(a[:rows], full[0][0][:rows])
         assert np.array_equal(l_[:rows].view(np.int32), full[0][1][:rows].view(np.int32))
-    judge(xs, full[0][0], full[0][1], share_oracle(xs, ranks, 1), f"share {ranks} ranks cap 20")
+    check_outputs(xs, full[0][0], full[0][1], share_oracle(xs, ranks, 1), f"share {ranks} ranks cap 20")
     assert int(ws[:512].count_nonzero()) == 0
 
 
