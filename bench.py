@@ -309,16 +309,22 @@ def main():
         w0, wr0 = copies[0]
 
         def t_call(fn, reps):
-            for _ in range(10):
+            # the first calls after the decode phase run slower (clocks rise
+            # under the compute-bound GEMMs): warm up for about 12 ms, then
+            # take the median of three timed windows
+            for _ in range(40):
                 fn()
             torch.cuda.synchronize()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            for _ in range(reps):
-                fn()
-            e.record()
-            torch.cuda.synchronize()
-            return s.elapsed_time(e) / reps * 1000.0
+            times = []
+            for _ in range(3):
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                for _ in range(reps):
+                    fn()
+                e.record()
+                torch.cuda.synchronize()
+                times.append(s.elapsed_time(e) / reps * 1000.0)
+            return sorted(times)[1]
 
         # the whole chunk first (it is the reported figure), then its pieces
         t_all = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
