@@ -481,13 +481,17 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
 // Row group: rows r0..r0+3 (those below `rows`). Every logit is stored; for
 // the fused call wave w selects the top-16 of row r0 + w, reading the logits
 // with coherent loads (other workgroups of this launch wrote them).
-__device__ void row_group(const DecodeArgs& a, const int r0, char* smem) {
+// `after_loads` runs in the waves that select (wave 0 always does), once their
+// logit loads are issued.
+template <class AfterLoads>
+__device__ void row_group(const DecodeArgs& a, const int r0, char* smem, AfterLoads after_loads) {
   uint64_t* scratch = reinterpret_cast<uint64_t*>(smem);
   const int nr = min(kRowGroup, a.rows - r0);
   const int w = threadIdx.x >> 6;
   if (w < nr)
     topk16_wave<true>(a.logits + (size_t)(r0 + w) * kExperts, a.ids + (size_t)(r0 + w) * kTopK,
-                      a.weights + (size_t)(r0 + w) * kTopK, scratch + w * kTopkScratch);
+                      a.weights + (size_t)(r0 + w) * kTopK, scratch + w * kTopkScratch,
+                      after_loads);
   __syncthreads();
 }
 
@@ -561,10 +565,17 @@ void decode_route_kernel(DecodeArgs a) {
   }
   int r = !a.fuse_topk ? -1 : router_done ? 0 : claim_rows<Sh>(a, false, pair, &slot);
   while (r >= 0) {
-    row_group(a, r, smem);
-    // groups are handed out in order: none is left after the one that ends
-    // at or past the last row (and the router is known complete by now)
-    r = r + kRowGroup < a.rows ? claim_rows<Sh>(a, true, pair, &slot) : -1;
+    // Groups are handed out in order: none is left after the one that ends
+    // at or past the last row. Otherwise thread 0 claims the next group as
+    // soon as its wave's logit loads are issued: the claim's round trip then
+    // overlaps the selection, and (issued after the loads) it does not hold
+    // up the in-order wait for them.
+    const bool more = r + kRowGroup < a.rows;
+    uint32_t c = ~0u;
+    row_group(a, r, smem, [&] {
+      if (more && threadIdx.x == 0) c = kRowGroup + add_dev(&pair[1], (uint32_t)kRowGroup);
+    });
+    r = broadcast(threadIdx.x == 0 && c < (uint32_t)a.rows ? (int)c : -1, &slot);
   }
   if (router_done && threadIdx.x == 0) {
     uint32_t* other = &a.counters[Sh::CtrPair + 2 * (par ^ 1u)];
