@@ -495,22 +495,18 @@ __device__ void row_group(const DecodeArgs& a, const int r0, char* smem, AfterLo
   __syncthreads();
 }
 
-// Claim the next group of rows. Group 0 (rows 0..3) belongs to the workgroup
-// that completed the router, which starts on it without a claim; pair[1]
-// hands out the later groups. A latent workgroup first reads the pair in one
-// coherent load and claims only if the router is complete and a group is
-// left. Returns the group's first row, or -1. Thread 0 holds `pair`.
+// A latent workgroup's first claim of a row group. Group 0 (rows 0..3)
+// belongs to the workgroup that completed the router, which starts on it
+// without a claim; pair[1] hands out the later groups. The latent workgroup
+// first reads the pair in one coherent load and claims only if the router is
+// complete and a group is left. Returns the group's first row, or -1. Thread
+// 0 holds `pair`.
 template <class Sh>
-__device__ __forceinline__ int claim_rows(const DecodeArgs& a, bool router_done, uint32_t* pair,
-                                          int* slot) {
+__device__ __forceinline__ int first_claim(const DecodeArgs& a, uint32_t* pair, int* slot) {
   int r = -1;
   if (threadIdx.x == 0) {
-    bool go = router_done;
-    if (!go) {
-      const uint64_t v = ld_dev(reinterpret_cast<const uint64_t*>(pair));
-      go = (uint32_t)v == (uint32_t)Sh::RtTiles && kRowGroup + (uint32_t)(v >> 32) < (uint32_t)a.rows;
-    }
-    if (go) {
+    const uint64_t v = ld_dev(reinterpret_cast<const uint64_t*>(pair));
+    if ((uint32_t)v == (uint32_t)Sh::RtTiles && kRowGroup + (uint32_t)(v >> 32) < (uint32_t)a.rows) {
       const uint32_t c = kRowGroup + add_dev(&pair[1], (uint32_t)kRowGroup);
       if (c < (uint32_t)a.rows) r = (int)c;
     }
@@ -563,7 +559,7 @@ void decode_route_kernel(DecodeArgs a) {
     if (router_done && threadIdx.x == 0) st_dev(&pair[0], 0u);
     return;
   }
-  int r = !a.fuse_topk ? -1 : router_done ? 0 : claim_rows<Sh>(a, false, pair, &slot);
+  int r = !a.fuse_topk ? -1 : router_done ? 0 : first_claim<Sh>(a, pair, &slot);
   while (r >= 0) {
     // Groups are handed out in order: none is left after the one that ends
     // at or past the last row. Otherwise thread 0 claims the next group as
