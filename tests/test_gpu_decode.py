@@ -161,3 +161,28 @@ def test_run_call_validation_launches_nothing():
     torch.cuda.synchronize()
     assert (bits_host(o.latent) == 0xFFFF).all()
     assert int(ws.count_nonzero()) == 0
+
+
+def test_zero_rows_degenerate_case():
+    """All-zero hidden rows among ordinary ones: their latent is +0.0, their
+    logits are all 0.0, so the top-16 is experts 0..15 (lowest index on the
+    896-way tie) with weights exactly 1/16; the other rows are unaffected."""
+    log("decode with all-zero hidden rows")
+    w, wr = weights_dev(0)
+    for width in (8, 20):
+        xs = gen.hidden(width, bank=90 + width)
+        zero = [1, width - 1] if width == 8 else [0, 7, 16, 19]
+        xs[zero] = 0
+        plan = route.Plan(route.MODE_DECODE, width)
+        ws = plan.new_workspace()
+        o = Outputs(width)
+        o.poison()
+        route.fused(plan, bf16_dev(xs), w, wr, o.latent, o.logits, o.ids, o.weights, ws)
+        torch.cuda.synchronize()
+        h = o.host()
+        for r in zero:
+            assert (h["latent"][r] == 0).all()
+            assert (h["logits"][r].view(np.uint32) == 0).all()
+            assert np.array_equal(h["ids"][r], np.arange(16))
+            assert (h["weights"][r] == np.float32(1.0 / 16.0)).all()
+        check_outputs(xs, h, f"decode w={width} with zero rows")
