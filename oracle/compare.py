@@ -59,7 +59,7 @@ def bf16_spacing(bits: np.ndarray) -> np.ndarray:
 
 
 def latent_check(got_bits, ref_bits, exact, abs_terms) -> dict:
-    """Judge BF16 latent bits against the oracle (see module docstring)."""
+    """Check BF16 latent bits against the oracle (see module docstring)."""
     got_bits = np.asarray(got_bits, dtype=np.uint16)
     d = bf16_ulp_distance(got_bits, ref_bits)
     within = d <= 1
@@ -85,7 +85,7 @@ def f32_spacing(v: np.ndarray) -> np.ndarray:
 
 
 def logits_check(got, ref, exact, abs_terms, c: float = 1.0) -> dict:
-    """Judge FP32 logits: within 1 ULP of the correctly rounded value, or
+    """Check FP32 logits: within 1 ULP of the correctly rounded value, or
     |got - exact| <= ulp(got)/2 + c * 2**-24 * sum_k |x_k Wr_k| (the error any
     summation of FP32-rounded partial sums can reach when a logit is small
     against the magnitude of its terms)."""
@@ -100,7 +100,9 @@ def logits_check(got, ref, exact, abs_terms, c: float = 1.0) -> dict:
         "band": int(((~within) & band_ok).sum()),
         "fail": int(((~within) & (~band_ok)).sum()),
         "max_ulp": int(d.max()) if d.size else 0,
-        "max_err_over_terms": float((err / (U32 * abs_terms)).max()) if d.size else 0.0,
+        # (outputs whose terms are all zero have no scale and are left out)
+        "max_err_over_terms": float((err[abs_terms > 0] / (U32 * abs_terms[abs_terms > 0])).max())
+        if (abs_terms > 0).any() else 0.0,
     }
 
 

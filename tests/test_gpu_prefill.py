@@ -83,3 +83,19 @@ def test_prefill_fused_equals_two_calls():
     for k in ("latent", "logits", "ids"):
         assert np.array_equal(a[k], b[k]), k
     assert np.array_equal(a["weights"].view(np.uint32), b["weights"].view(np.uint32))
+
+
+def test_prefill_zero_rows_degenerate_case():
+    """All-zero hidden rows inside a ragged chunk (200 rows, tile edges at 192):
+    latent +0.0, logits all 0.0, ids 0..15, weights exactly 1/16."""
+    log("prefill with all-zero hidden rows")
+    xs = gen.hidden(200, bank=95, outliers=True)
+    zero = [0, 100, 191, 192, 199]
+    xs[zero] = 0
+    got = run_prefill(xs, cap=256, fused=True)
+    for r in zero:
+        assert (got["latent"][r] == 0).all()
+        assert (got["logits"][r].view(np.uint32) == 0).all()
+        assert np.array_equal(got["ids"][r], np.arange(16))
+        assert (got["weights"][r] == np.float32(1.0 / 16.0)).all()
+    check_outputs(xs, got, "prefill rows=200 with zero rows")
