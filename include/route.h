@@ -21,7 +21,8 @@
  *       top-16" (voipmonitor/flare pull request 24), "What / why" and
  *       "Dependency".
  *
- * Envelope: a plan is prepared once for a mode and a row capacity; decode
+ * Envelope: a plan is prepared once for a mode, a row capacity and an output
+ * shape (the whole route, or a rank share below); decode
  * plans accept 1..20 rows (the same page, "What / why": rounds of 1..20 rows
  * are prepared, anything else raises at preparation), prefill plans 1..3072
  * rows (the 3072-row chunk of pull request 16's timing table). There is no
@@ -60,9 +61,9 @@
  * and latent/logits have that many columns. Each output is still one full-K
  * dot product rounded once, within the same bounds as the whole route's (the
  * K split differs, so the last bit may differ from the whole route's
- * corresponding column). A share has no top-16
- * (its experts are a fraction of the route's): route_topk16, route_fused and
- * route_topk16_sharded return ROUTE_E_SHAPE on a share plan.
+ * corresponding column). A share has no top-16 (its experts are a fraction
+ * of the route's): route_topk16, route_fused and route_topk16_sharded return
+ * ROUTE_E_SHAPE on a share plan.
  *
  * `stream` is a hipStream_t (NULL = the null stream); the current HIP device
  * must be the plan's device.
