@@ -154,6 +154,47 @@ int route_fused(const route_plan* plan, const void* x, const void* w_latent,
 int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t shards, int32_t* ids,
                          float* weights, void* workspace, int32_t rows, void* stream);
 
+/* Packed weights. Weights are model parameters, loaded once; each kernel
+ * reads them fastest in an order of its own, so route_pack_weights reorders
+ * both weights once into the plan's packed format, and the *_packed calls
+ * then read that buffer in place of w_latent and w_router. Their results are
+ * bitwise those of route_latent_router / route_fused on the original weights:
+ * every kernel lane receives the same operand values in the same order; only
+ * the loads change.
+ *   decode (whole route): both weights in the decode kernel's consumption
+ *     order, so every workgroup streams one contiguous block with 16-byte
+ *     loads (the [K][N] layouts give it strided 128-byte row segments);
+ *     77,070,336 bytes: the latent weight's 51,380,224 bytes of BF16 values,
+ *     then the router weight's 25,690,112 bytes of FP32 values;
+ *   prefill: the weights K-contiguous, W as [3584][7168] BF16 (the [out][in]
+ *     layout of a linear layer) and the router weight as its three exact
+ *     BF16 parts [2688][7168] (split once here instead of on every call), so
+ *     the GEMMs read both operands with 16-byte LDS reads; 89,915,392 bytes.
+ * Share plans have no packed format: route_packed_weight_bytes returns 0 and
+ * the packed calls return ROUTE_E_SHAPE. */
+
+/* Bytes of the plan's packed buffer (decode 77,070,336, prefill 89,915,392),
+ * or 0 for a NULL or share plan. */
+size_t route_packed_weight_bytes(const route_plan* plan);
+
+/* Write the packed buffer `packed` (caller-owned, route_packed_weight_bytes
+ * bytes, 16-byte aligned) from w_latent [7168][3584] BF16 and w_router
+ * [7168][896] FP32; enqueued on `stream`. Every pointer is required; the
+ * buffer must not overlap the weights. A decode buffer serves decode plans
+ * and a prefill buffer prefill plans, of any row capacity. */
+int route_pack_weights(const route_plan* plan, const void* w_latent, const float* w_router,
+                       void* packed, void* stream);
+
+/* route_latent_router with packed weights. */
+int route_latent_router_packed(const route_plan* plan, const void* x, const void* packed,
+                               void* latent, float* logits, void* workspace, int32_t rows,
+                               void* stream);
+
+/* route_fused with packed weights (`logits` may be NULL). */
+int route_fused_packed(const route_plan* plan, const void* x, const void* packed, void* latent,
+                       float* logits, int32_t* ids, float* weights, void* workspace, int32_t rows,
+                       void* stream);
+
 /* Free a plan (NULL is accepted). */
 void route_destroy(route_plan* plan);
 

@@ -206,7 +206,7 @@ constexpr int kTailRows = kDecodeMaxRows - 16;
 
 // Returns true in the workgroup that combined the last router tile: every
 // logit of every row is then stored.
-template <int NT, class Sh>
+template <int NT, class Sh, bool Packed>
 __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* slot, uint32_t* pair) {
   constexpr bool kTail = NT == 2;                     // rows 16..19 on the VALU
   const int wave = threadIdx.x >> 6;
@@ -223,7 +223,11 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   const int k0 = split * Sh::KR + wave * Sh::KRWave;
   // lanes past the last expert of a share read a valid pair; never stored
   const int ecol = Sh::E % kRtTileE == 0 ? e0 + 2 * m : min(e0 + 2 * m, Sh::E - 2);
-  const float* wp = a.wr + (size_t)(k0 + 4 * g) * Sh::E + ecol;
+  // packed: the unit's 4 waves' blocks are contiguous, a wave's steps are
+  // 512-float blocks, and lane l's two 16-byte pieces of a step sit at l and
+  // 64 + l (see pack_router_kernel)
+  const float* wp = Packed ? a.wr + (size_t)u * (Sh::KR * kRtTileE) + wave * (Sh::KRWave * kRtTileE) + 4 * lane
+                           : a.wr + (size_t)(k0 + 4 * g) * Sh::E + ecol;
 
   // LDS after the reduction buffer: hidden rows 16..19 over the unit's K chunk
   uint16_t* xt = reinterpret_cast<uint16_t*>(smem + kWaves * kRowsPad * kRtTileE * 8);
@@ -246,10 +250,19 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   f32x2 wv[kDepthR][4];
   u32x2 xv[kDepthR];
   auto issue = [&](int st) {
+    if constexpr (Packed) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wv[st % kDepthR][j] =
-          __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStepR + j) * Sh::E));
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 v = __builtin_nontemporal_load((const f32x4*)(wp + st * (kStepR * kRtTileE) + h * 256));
+        wv[st % kDepthR][2 * h] = f32x2{v[0], v[1]};
+        wv[st % kDepthR][2 * h + 1] = f32x2{v[2], v[3]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wv[st % kDepthR][j] =
+            __builtin_nontemporal_load((const f32x2*)(wp + (size_t)(st * kStepR + j) * Sh::E));
+    }
     xv[st % kDepthR] = *(const u32x2*)(a.x + (size_t)xr[0] * kHidden + k0 + 4 * g + st * kStepR);
   };
   // up to 7 steps of loads in flight: all of them for the whole route
@@ -366,7 +379,7 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   return publish(&pair[0], slot) == (uint32_t)(Sh::RtTiles - 1);
 }
 
-template <int NT, class Sh>
+template <int NT, class Sh, bool Packed>
 __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* slot) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -382,7 +395,11 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   const int k0 = split * Sh::KL + wave * Sh::KLWave;
   // lanes past the last column of a share read a valid quad; never stored
   const int ncol = Sh::N % kLatTileN == 0 ? n0 + 4 * m : min(n0 + 4 * m, Sh::N - 4);
-  const uint16_t* wp = a.w + (size_t)(k0 + 8 * g) * Sh::N + ncol;
+  // packed: the unit's 4 waves' blocks are contiguous, a wave's steps are
+  // 2048-value blocks, and lane l's piece for MFMA c sits at 64 c + l (see
+  // pack_latent_kernel)
+  const uint16_t* wp = Packed ? a.w + (size_t)u * (Sh::KL * kLatTileN) + wave * (Sh::KLWave * kLatTileN) + 8 * lane
+                              : a.w + (size_t)(k0 + 8 * g) * Sh::N + ncol;
 
   f32x4 acc[NT][4];
 #pragma unroll
@@ -391,12 +408,20 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
     for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kDepth = depth<NT>() < Sh::StepsL ? depth<NT>() : Sh::StepsL;
   u32x2 wv[kDepth][8];
+  u32x4 wq[kDepth][4];
   u32x4 xv[kDepth][NT];
   auto issue = [&](int st) {
+    if constexpr (Packed) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wv[st % kDepth][j] =
-          __builtin_nontemporal_load((const u32x2*)(wp + (size_t)(st * kStepL + j) * Sh::N));
+      for (int c = 0; c < 4; ++c)
+        wq[st % kDepth][c] =
+            __builtin_nontemporal_load((const u32x4*)(wp + st * (kStepL * kLatTileN) + c * 512));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        wv[st % kDepth][j] =
+            __builtin_nontemporal_load((const u32x2*)(wp + (size_t)(st * kStepL + j) * Sh::N));
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       xv[st % kDepth][nt] = *(const u32x4*)(a.x + (size_t)xr[nt] * kHidden + k0 + 8 * g + st * kStepL);
@@ -411,9 +436,13 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
     for (int c = 0; c < 4; ++c) {
       const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
       u32x4 av;
+      if constexpr (Packed) {
+        av = wq[q][c];
+      } else {
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        av[p] = __builtin_amdgcn_perm(wv[q][2 * p + 1][c >> 1], wv[q][2 * p][c >> 1], sel);
+        for (int p = 0; p < 4; ++p)
+          av[p] = __builtin_amdgcn_perm(wv[q][2 * p + 1][c >> 1], wv[q][2 * p][c >> 1], sel);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         acc[nt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -529,9 +558,10 @@ __device__ __forceinline__ int first_claim(const DecodeArgs& a, uint32_t* pair, 
 // combined, so every increment of this call's router counter lands in this
 // call's pair; a latent workgroup that read the flipped parity would only
 // find a cleared pair and take no row.
-template <int NT, class Sh>
+template <int NT, class Sh, bool Packed>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_route_kernel(DecodeArgs a) {
+  static_assert(!Packed || Sh::kFull, "packed weights cover the whole route");
   constexpr int kLatBytes = kWaves * rows_kept<NT>() * kLatTileN * 4;
   constexpr int kRtBytes = kWaves * rows_kept<NT>() * kRtTileE * 8 +
                            (NT == 2 ? kTailRows * Sh::KR * 2 : 0);   // + staged hidden rows
@@ -547,9 +577,9 @@ void decode_route_kernel(DecodeArgs a) {
   uint32_t* pair = &a.counters[Sh::CtrPair + 2 * par];
   bool router_done = false;
   if (b < Sh::RtUnits) {
-    router_done = router_unit<NT, Sh>(a, b, smem, &slot, pair);
+    router_done = router_unit<NT, Sh, Packed>(a, b, smem, &slot, pair);
     if (!router_done) return;
-  } else if (!latent_unit<NT, Sh>(a, b - Sh::RtUnits, smem, &slot)) {
+  } else if (!latent_unit<NT, Sh, Packed>(a, b - Sh::RtUnits, smem, &slot)) {
     return;
   }
   if constexpr (!Sh::kFull) {
@@ -612,22 +642,22 @@ size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off
   return ws_bytes<FullShape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
 }
 
-template <class Sh>
+template <class Sh, bool Packed = false>
 static void launch_shape(const DecodeArgs& a, int rows, hipStream_t stream) {
   if (rows <= 16)
-    hipLaunchKernelGGL((decode_route_kernel<1, Sh>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_route_kernel<1, Sh, Packed>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_route_kernel<2, Sh>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_route_kernel<2, Sh, Packed>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
                                const DecodeWorkspace& ws, int rows, int rows_cap, int n_latent,
-                               int n_experts, bool fuse_topk, hipStream_t stream) {
+                               int n_experts, bool fuse_topk, bool packed, hipStream_t stream) {
   if (rows < 1 || rows > kDecodeMaxRows || rows > rows_cap) return hipErrorInvalidValue;
   if (!decode_shape_valid(n_latent, n_experts)) return hipErrorInvalidValue;
   const bool full = n_latent == FullShape::N;
-  if (fuse_topk && !full) return hipErrorInvalidValue;
+  if ((fuse_topk || packed) && !full) return hipErrorInvalidValue;
   DecodeArgs a;
   a.x = x;
   a.w = w_latent;
@@ -642,12 +672,95 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (full)
+  if (full && packed)
+    launch_shape<FullShape, true>(a, rows, stream);
+  else if (full)
     launch_shape<FullShape>(a, rows, stream);
   else if (n_latent == Tp8Shape::N)
     launch_shape<Tp8Shape>(a, rows, stream);
   else
     launch_shape<Tp16Shape>(a, rows, stream);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ weight packing --
+//
+// The packed decode weights hold the same values as W [7168][3584] BF16 and
+// Wr [7168][896] FP32, reordered once (at weight load) into the order in which
+// the whole-route kernel's lanes consume them, so that every unit streams one
+// contiguous block and every load instruction covers 1 KB with one 16-byte
+// piece per lane. The kernel's operands, and so its results, are bitwise those
+// of the [K][N] layout.
+//
+// Latent: unit u (tile u mod 56, K split u / 56), wave w, step s, MFMA c, lane
+// (g, m) = (l / 16, l mod 16): 8 BF16 values W[k + i][n], i = 0..7, with
+// k = split*1792 + w*448 + 32 s + 8 g and n = tile*64 + 4 m + c, at value
+// offset ((((u*4 + w)*14 + s)*4 + c)*64 + l)*8.
+// Router: unit u (tile u mod 28, K split u / 28), wave w, step s, half h, lane
+// (g, m): {Wr[k][e], Wr[k][e+1], Wr[k+1][e], Wr[k+1][e+1]} with
+// k = split*448 + w*112 + 16 s + 4 g + 2 h and e = tile*32 + 2 m, at float
+// offset ((((u*4 + w)*7 + s)*2 + h)*64 + l)*4.
+using PackShape = FullShape;
+constexpr int kPackLatPieces = kHidden * kLatent / 8;    // 16-byte pieces
+constexpr int kPackRtPieces = kHidden * kExperts / 4;
+
+__global__ __launch_bounds__(256) void pack_latent_kernel(const uint16_t* __restrict__ w,
+                                                          uint16_t* __restrict__ out) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= kPackLatPieces) return;
+  const int l = p % 64;
+  const int c = (p / 64) % 4;
+  const int s = (p / 256) % PackShape::StepsL;
+  const int wv = (p / (256 * PackShape::StepsL)) % kWaves;
+  const int u = p / (256 * PackShape::StepsL * kWaves);
+  const int tile = u % PackShape::LatTiles;
+  const int split = u / PackShape::LatTiles;
+  const int k = split * PackShape::KL + wv * PackShape::KLWave + kStepL * s + 8 * (l >> 4);
+  const int n = tile * kLatTileN + 4 * (l & 15) + c;
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = (uint32_t)w[(size_t)(k + 2 * i) * kLatent + n] |
+           ((uint32_t)w[(size_t)(k + 2 * i + 1) * kLatent + n] << 16);
+  *(u32x4*)(out + (size_t)p * 8) = v;
+}
+
+__global__ __launch_bounds__(256) void pack_router_kernel(const float* __restrict__ wr,
+                                                          float* __restrict__ out) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= kPackRtPieces) return;
+  const int l = p % 64;
+  const int h = (p / 64) % 2;
+  const int s = (p / 128) % PackShape::StepsR;
+  const int wv = (p / (128 * PackShape::StepsR)) % kWaves;
+  const int u = p / (128 * PackShape::StepsR * kWaves);
+  const int tile = u % PackShape::RtTiles;
+  const int split = u / PackShape::RtTiles;
+  const int k = split * PackShape::KR + wv * PackShape::KRWave + kStepR * s + 4 * (l >> 4) + 2 * h;
+  const int e = tile * kRtTileE + 2 * (l & 15);
+  const f32x2 r0 = *(const f32x2*)(wr + (size_t)k * kExperts + e);
+  const f32x2 r1 = *(const f32x2*)(wr + (size_t)(k + 1) * kExperts + e);
+  *(f32x4*)(out + (size_t)p * 4) = f32x4{r0[0], r0[1], r1[0], r1[1]};
+}
+
+static_assert((size_t)kPackLatPieces * 16 == (size_t)PackShape::LatUnits * kWaves * PackShape::StepsL * 4 * 64 * 16,
+              "the latent pieces cover every unit, wave, step, MFMA and lane");
+static_assert((size_t)kPackRtPieces * 16 == (size_t)PackShape::RtUnits * kWaves * PackShape::StepsR * 2 * 64 * 16,
+              "the router pieces cover every unit, wave, step, half and lane");
+
+size_t decode_packed_latent_bytes() { return (size_t)kHidden * kLatent * 2; }
+size_t decode_packed_bytes() { return decode_packed_latent_bytes() + (size_t)kHidden * kExperts * 4; }
+
+hipError_t launch_pack_decode_weights(const uint16_t* w_latent, const float* w_router, void* packed,
+                                      hipStream_t stream) {
+  uint16_t* lat = static_cast<uint16_t*>(packed);
+  float* rt = reinterpret_cast<float*>(static_cast<char*>(packed) + decode_packed_latent_bytes());
+  hipLaunchKernelGGL(pack_latent_kernel, dim3((kPackLatPieces + 255) / 256), dim3(256), 0, stream,
+                     w_latent, lat);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_router_kernel, dim3((kPackRtPieces + 255) / 256), dim3(256), 0, stream,
+                     w_router, rt);
   return hipGetLastError();
 }
 

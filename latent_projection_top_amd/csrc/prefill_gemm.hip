@@ -42,6 +42,15 @@
 //     address, j = 0..3). The two 32-byte halves of a 64-byte row are swapped
 //     when (k >> 3) is odd, so the two lane groups of one read phase use
 //     different banks.
+//
+// Packed weights (BT = true): the weights stored K-contiguous instead, W as
+// [3584][7168] and the router's three BF16 parts as [2688][7168] (the parts
+// split once, when the weights are packed, in the same column order). The B
+// stage is then laid out like the A stage, [cols][64 k] with the same piece
+// swizzle, and read with ds_read_b128 like A: twice the bytes per LDS read
+// instruction of the transposing read. Every lane receives the same operand
+// values in the same order as with the [K][N] weights, so the results are
+// bitwise the same.
 #include "route_device.h"
 #include "route_launch.h"
 
@@ -132,7 +141,7 @@ __device__ __forceinline__ s16x4 lds_tr16(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
 }
 
-template <bool Router>
+template <bool Router, bool BT>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                          void* __restrict__ out, int rows, int mtiles) {
@@ -165,17 +174,28 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
 
   // ---- global -> LDS loads: load c of a stage (wave c % 8) -----------------
   //   c < A_LOADS: A rows 8 c .. 8 c + 7;  else B block (c - A_LOADS) / 4,
-  //   k rows 16 ((c - A_LOADS) % 4) .. + 15.
+  //   k rows 16 ((c - A_LOADS) % 4) .. + 15 ([K][N] weights), or B columns
+  //   8 (c - A_LOADS) .. + 7 (K-contiguous weights, laid out like A).
   const bool full_wave = wave + kGWaves * (S::PER_WAVE - 1) < S::LOADS;
-  uint32_t off[S::PER_WAVE];
+  // K-contiguous B: load i of a wave reads columns 64 (i - A_LOADS / 8) past
+  // those of its first B load, with the same piece swizzle, so one offset
+  // serves all of them and the column step goes on the scalar base
+  constexpr int kAW = S::A_LOADS / kGWaves;             // A loads per wave
+  constexpr size_t kBtStep = (size_t)kGWaves * 8 * kHidden * 2;
+  uint32_t off[BT ? kAW + 1 : S::PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < S::PER_WAVE; ++i) {
+  for (int i = 0; i < (BT ? kAW + 1 : S::PER_WAVE); ++i) {
     const int c = wave + kGWaves * i;
     if (c < S::A_LOADS) {
       const int r = 8 * c + (lane >> 3);
       const int piece = (lane & 7) ^ ((r >> 1) & 7);
       const int row = min(bm0 + r, rows - 1);
       off[i] = (uint32_t)(row * kHidden + 8 * piece) * 2u;
+    } else if constexpr (BT) {
+      const int ib = min(c, S::LOADS - 1) - S::A_LOADS;
+      const int r = 8 * ib + (lane >> 3);
+      const int piece = (lane & 7) ^ ((r >> 1) & 7);
+      off[i] = (uint32_t)((bn0 + r) * kHidden + 8 * piece) * 2u;
     } else {
       const int ib = min(c, S::LOADS - 1) - S::A_LOADS;
       const int k = 16 * (ib & 3) + (lane >> 2);
@@ -190,14 +210,18 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (kt % kGStages) * S::STAGE;
     const char* ab = a_src + (size_t)kt * (kGBK * 2);
-    const char* bb = b_src + (size_t)kt * ((size_t)kGBK * S::N * 2);
+    const char* bb = b_src + (BT ? (size_t)kt * (kGBK * 2) : (size_t)kt * ((size_t)kGBK * S::N * 2));
 #pragma unroll
     for (int i = 0; i < S::PER_WAVE; ++i) {
       const int c = wave + kGWaves * i;
-      if (i < S::A_LOADS / kGWaves)
+      if (i < kAW)
         dma16(ab, off[i], st + c * 1024);
-      else if (c < S::LOADS)
-        dma16(bb, off[i], st + c * 1024);
+      else if (c < S::LOADS) {
+        if constexpr (BT)
+          dma16(bb + (size_t)(i - kAW) * kBtStep, off[kAW], st + c * 1024);
+        else
+          dma16(bb, off[i], st + c * 1024);
+      }
     }
   };
 
@@ -222,12 +246,26 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     bf16x8 b[S::NT];
   };
   auto read_a = [&](uint32_t st, int s, int i) { return lds_b128(st + a_rd[s] + 2048 * i); };
-  auto read_b = [&](uint32_t st, int s, int j) {
-    const int col = tile_col<Router>(wn, j);
-    const uint32_t base = st + b_rd[(col >> 4) & 1] + (col >> 5) * 4096 + 32 * s * 64;
-    const s16x4 lo = lds_tr16(base);
-    const s16x4 hi = lds_tr16(base + 4 * 64);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  // K-contiguous B, column c of the block, K half s: like A, row c (a multiple
+  // of 16 plus m), piece 4 s + g
+  // (the wave's column offset goes into the base, so that every tile's
+  // offset is a constant the read instruction carries)
+  uint32_t bt_rd[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    bt_rd[s] = (uint32_t)(S::A_BYTES + (tile_col<Router>(wn, 0) + m) * 128 +
+                          (((4 * s + g) ^ ((m >> 1) & 7)) * 16));
+  auto read_b = [&](uint32_t st, int s, int j) -> bf16x8 {
+    if constexpr (BT) {
+      // tile_col(wn, j) = tile_col(wn, 0) + tile_col(0, j)
+      return lds_b128(st + bt_rd[s] + 128 * tile_col<Router>(0, j));
+    } else {
+      const int col = tile_col<Router>(wn, j);
+      const uint32_t base = st + b_rd[(col >> 4) & 1] + (col >> 5) * 4096 + 32 * s * 64;
+      const s16x4 lo = lds_tr16(base);
+      const s16x4 hi = lds_tr16(base + 4 * 64);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
   auto stage_lds = [&](int kt) { return lds0 + (kt % kGStages) * S::STAGE; };
 
@@ -269,10 +307,8 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
                                                                restart ? zero4 : chain[i][j], 0, 0, 0);
         }
         if (reload && i == S::MT - 1) o.b[j] = read_b(st_n, s_n, j);
-        // SB1
       }
       if (reload) o.a[i] = read_a(st_n, s_n, i);
-      // SB2
     }
   };
 
@@ -346,6 +382,16 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   }
 }
 
+// The three exact BF16 parts of an FP32 weight: each takes the top 8
+// significant bits (nearest-even) of what the previous ones leave.
+__device__ __forceinline__ void split3(float wv, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_rne(wv);
+  const float r1 = wv - __uint_as_float(hi << 16);
+  mid = f32_to_bf16_rne(r1);
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  lo = f32_to_bf16_rne(r2);
+}
+
 // Split the FP32 router weight into its three exact BF16 parts, stored as
 // parts[k][e / 64][p][e % 64]. One thread per 8 consecutive experts of a row.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
@@ -360,11 +406,8 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const float wv = c < 4 ? v0[c] : v1[c - 4];
-    const uint32_t hi = f32_to_bf16_rne(wv);
-    const float r1 = wv - __uint_as_float(hi << 16);
-    const uint32_t mid = f32_to_bf16_rne(r1);
-    const float r2 = r1 - __uint_as_float(mid << 16);
-    const uint32_t lo = f32_to_bf16_rne(r2);
+    uint32_t hi, mid, lo;
+    split3(wv, hi, mid, lo);
     const int sh = (c & 1) * 16;
     if ((c & 1) == 0) p[0][c >> 1] = p[1][c >> 1] = p[2][c >> 1] = 0u;
     p[0][c >> 1] |= hi << sh;
@@ -375,6 +418,57 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 #pragma unroll
   for (int q = 0; q < 3; ++q)
     *(u32x4*)(dst + 64 * q) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
+}
+
+// Packing for the K-contiguous GEMM variant, once per weight set, through
+// 32 x 32 LDS tiles: W [7168][3584] -> WT [3584][7168]; Wr [7168][896] ->
+// its three BF16 parts as partsT [2688][7168], part p of expert e in row
+// (e / 64) * 192 + 64 p + e % 64 (the column order of the [K][N] parts).
+__global__ __launch_bounds__(256) void pack_prefill_latent_kernel(const uint16_t* __restrict__ w,
+                                                                  uint16_t* __restrict__ wt) {
+  __shared__ uint16_t tile[32][34];
+  const int n0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tile[ty + 8 * i][tx] = w[(size_t)(k0 + ty + 8 * i) * kLatent + n0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wt[(size_t)(n0 + ty + 8 * i) * kHidden + k0 + tx] = tile[tx][ty + 8 * i];
+}
+
+__global__ __launch_bounds__(256) void pack_prefill_router_kernel(const float* __restrict__ wr,
+                                                                  uint16_t* __restrict__ parts_t) {
+  __shared__ float tile[32][33];
+  const int e0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tile[ty + 8 * i][tx] = wr[(size_t)(k0 + ty + 8 * i) * kExperts + e0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + ty + 8 * i;
+    uint32_t p[3];
+    split3(tile[tx][ty + 8 * i], p[0], p[1], p[2]);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      parts_t[(size_t)((e / 64) * 192 + 64 * q + e % 64) * kHidden + k0 + tx] = (uint16_t)p[q];
+  }
+}
+
+size_t prefill_packed_latent_bytes() { return (size_t)kLatent * kHidden * 2; }
+size_t prefill_packed_bytes() { return prefill_packed_latent_bytes() + (size_t)kRouterCols * kHidden * 2; }
+
+hipError_t launch_pack_prefill_weights(const uint16_t* w_latent, const float* w_router, void* packed,
+                                       hipStream_t stream) {
+  uint16_t* wt = static_cast<uint16_t*>(packed);
+  uint16_t* parts_t = reinterpret_cast<uint16_t*>(static_cast<char*>(packed) + prefill_packed_latent_bytes());
+  hipLaunchKernelGGL(pack_prefill_latent_kernel, dim3(kLatent / 32, kHidden / 32), dim3(256), 0, stream,
+                     w_latent, wt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_prefill_router_kernel, dim3(kExperts / 32, kHidden / 32), dim3(256), 0, stream,
+                     w_router, parts_t);
+  return hipGetLastError();
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -392,8 +486,24 @@ hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, ui
                                  int rows, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
   const int mt = (rows + kGBM - 1) / kGBM;
-  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(mt * (kLatent / 224)), dim3(kGThreads), 0,
+  hipLaunchKernelGGL((prefill_gemm_kernel<false, false>), dim3(mt * (kLatent / 224)), dim3(kGThreads), 0,
                      stream, x, w_latent, (void*)latent, rows, mt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t* latent, float* logits,
+                                 int rows, hipStream_t stream) {
+  if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
+  const uint16_t* wt = static_cast<const uint16_t*>(packed);
+  const uint16_t* parts_t =
+      reinterpret_cast<const uint16_t*>(static_cast<const char*>(packed) + prefill_packed_latent_bytes());
+  const int mt = (rows + kGBM - 1) / kGBM;
+  hipLaunchKernelGGL((prefill_gemm_kernel<false, true>), dim3(mt * (kLatent / 224)), dim3(kGThreads), 0,
+                     stream, x, wt, (void*)latent, rows, mt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((prefill_gemm_kernel<true, true>), dim3(mt * (kRouterCols / 192)), dim3(kGThreads), 0,
+                     stream, x, parts_t, (void*)logits, rows, mt);
   return hipGetLastError();
 }
 
@@ -403,7 +513,7 @@ hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint1
   hipLaunchKernelGGL(router_split_kernel, dim3(kHidden * (kExperts / 8) / 256), dim3(256), 0, stream,
                      w_router, parts);
   const int mt = (rows + kGBM - 1) / kGBM;
-  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), 0,
+  hipLaunchKernelGGL((prefill_gemm_kernel<true, false>), dim3(mt * (kRouterCols / 192)), dim3(kGThreads), 0,
                      stream, x, (const uint16_t*)parts, (void*)logits, rows, mt);
   return hipGetLastError();
 }

@@ -53,17 +53,27 @@ route::DecodeWorkspace decode_ws(const route_plan* p, void* ws) {
   return d;
 }
 
+int run_prefill_packed(const void* x, const void* packed, void* latent, float* logits, int32_t* ids,
+                       float* weights, int32_t rows, bool fused, hipStream_t s) {
+  int st = status_of(route::launch_prefill_packed(static_cast<const uint16_t*>(x), packed,
+                                                  static_cast<uint16_t*>(latent), logits, rows, s));
+  if (st != ROUTE_OK || !fused) return st;
+  return status_of(route::launch_topk16(logits, ids, weights, rows, s));
+}
+
 int run_latent_router(const route_plan* p, const void* x, const void* w_latent, const float* w_router,
                       void* latent, float* logits, int32_t* ids, float* weights, void* ws,
-                      int32_t rows, bool fused, hipStream_t s) {
+                      int32_t rows, bool fused, hipStream_t s, bool packed = false) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (packed && p->mode == ROUTE_MODE_PREFILL)
+    return run_prefill_packed(x, w_latent, latent, logits, ids, weights, rows, fused, s);
   const uint16_t* wb = static_cast<const uint16_t*>(w_latent);
   uint16_t* lb = static_cast<uint16_t*>(latent);
   if (p->mode == ROUTE_MODE_DECODE) {
     // decode: one launch; the fused select runs inside the projection kernel
     return status_of(route::launch_decode_route(xb, wb, w_router, lb, logits, ids, weights,
                                                 decode_ws(p, ws), rows, p->rows_cap, p->latent,
-                                                p->experts, fused, s));
+                                                p->experts, fused, packed, s));
   }
   int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, s));
   if (st != ROUTE_OK) return st;
@@ -71,6 +81,22 @@ int run_latent_router(const route_plan* p, const void* x, const void* w_latent, 
   st = status_of(route::launch_prefill_router(xb, w_router, parts, logits, rows, s));
   if (st != ROUTE_OK || !fused) return st;
   return status_of(route::launch_topk16(logits, ids, weights, rows, s));
+}
+
+// Packed weights serve whole-route plans (decode and prefill have their own
+// formats); a rank share has none.
+bool packed_plan(const route_plan* p) { return !is_share(p); }
+
+size_t packed_bytes(const route_plan* p) {
+  return p->mode == ROUTE_MODE_DECODE ? route::decode_packed_bytes() : route::prefill_packed_bytes();
+}
+
+// The decode packed buffer: latent values first, router values after them.
+// (The prefill GEMM launcher splits its own buffer.)
+const float* packed_router(const route_plan* p, const void* packed) {
+  if (p->mode != ROUTE_MODE_DECODE) return nullptr;
+  return reinterpret_cast<const float*>(static_cast<const char*>(packed) +
+                                        route::decode_packed_latent_bytes());
 }
 
 }  // namespace
@@ -171,6 +197,52 @@ int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t sh
   uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + plan->off_cand);
   return status_of(route::launch_topk16_sharded(logits, shards, ids, weights, cand, rows,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t route_packed_weight_bytes(const route_plan* plan) {
+  return plan && packed_plan(plan) ? packed_bytes(plan) : 0;
+}
+
+int route_pack_weights(const route_plan* plan, const void* w_latent, const float* w_router,
+                       void* packed, void* stream) {
+  if (!plan || !w_latent || !w_router || !packed) return ROUTE_E_ARG;
+  if (!packed_plan(plan)) return ROUTE_E_SHAPE;
+  if (misaligned(w_latent) || misaligned(w_router) || misaligned(packed)) return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  const uint16_t* wl = static_cast<const uint16_t*>(w_latent);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(plan->mode == ROUTE_MODE_DECODE ? route::launch_pack_decode_weights(wl, w_router, packed, s)
+                                                   : route::launch_pack_prefill_weights(wl, w_router, packed, s));
+}
+
+int route_latent_router_packed(const route_plan* plan, const void* x, const void* packed,
+                               void* latent, float* logits, void* workspace, int32_t rows,
+                               void* stream) {
+  if (!plan || !x || !packed || !latent || !logits || !workspace) return ROUTE_E_ARG;
+  if (!packed_plan(plan)) return ROUTE_E_SHAPE;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(x) || misaligned(packed) || misaligned(latent) || misaligned(logits) ||
+      misaligned(workspace))
+    return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  return run_latent_router(plan, x, packed, packed_router(plan, packed), latent, logits, nullptr, nullptr,
+                           workspace, rows, false, static_cast<hipStream_t>(stream), true);
+}
+
+int route_fused_packed(const route_plan* plan, const void* x, const void* packed, void* latent,
+                       float* logits, int32_t* ids, float* weights, void* workspace, int32_t rows,
+                       void* stream) {
+  if (!plan || !x || !packed || !latent || !ids || !weights || !workspace) return ROUTE_E_ARG;
+  if (!packed_plan(plan)) return ROUTE_E_SHAPE;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(x) || misaligned(packed) || misaligned(latent) || (logits && misaligned(logits)) ||
+      misaligned(ids) || misaligned(weights) || misaligned(workspace))
+    return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  float* lg = logits ? logits
+                     : reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_logits);
+  return run_latent_router(plan, x, packed, packed_router(plan, packed), latent, lg, ids, weights, workspace,
+                           rows, true, static_cast<hipStream_t>(stream), true);
 }
 
 void route_destroy(route_plan* plan) { delete plan; }

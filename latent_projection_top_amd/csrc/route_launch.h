@@ -24,7 +24,15 @@ size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_par
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
                                const DecodeWorkspace& ws, int rows, int rows_cap, int n_latent,
-                               int n_experts, bool fuse_topk, hipStream_t stream);
+                               int n_experts, bool fuse_topk, bool packed, hipStream_t stream);
+
+// Packed decode weights (whole route only): the latent weight's values
+// reordered into the decode kernel's consumption order, followed by the router
+// weight's, same byte counts as the [K][N] weights.
+size_t decode_packed_latent_bytes();
+size_t decode_packed_bytes();
+hipError_t launch_pack_decode_weights(const uint16_t* w_latent, const float* w_router, void* packed,
+                                      hipStream_t stream);
 
 hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,
                          hipStream_t stream);
@@ -43,5 +51,15 @@ hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, ui
 // parts: workspace for the three BF16 parts of w_router ([7168][2688] BF16)
 hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
                                  float* logits, int rows, hipStream_t stream);
+
+// Packed prefill weights: W as [3584][7168] BF16, then the router weight's
+// three exact BF16 parts as [2688][7168] (K contiguous); the GEMMs read them
+// with the same per-lane operands as the [K][N] path.
+size_t prefill_packed_latent_bytes();
+size_t prefill_packed_bytes();
+hipError_t launch_pack_prefill_weights(const uint16_t* w_latent, const float* w_router, void* packed,
+                                       hipStream_t stream);
+hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t* latent, float* logits,
+                                 int rows, hipStream_t stream);
 
 }  // namespace route

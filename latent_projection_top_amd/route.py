@@ -38,7 +38,8 @@ E_HIP = -6
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libroute.so")
 
 SYMBOLS = ("route_prepare", "route_workspace_bytes", "route_latent_router", "route_topk16",
-           "route_fused", "route_topk16_sharded", "route_destroy", "route_strerror")
+           "route_fused", "route_topk16_sharded", "route_packed_weight_bytes", "route_pack_weights",
+           "route_latent_router_packed", "route_fused_packed", "route_destroy", "route_strerror")
 
 
 class RouteError(RuntimeError):
@@ -71,6 +72,14 @@ def _load() -> ctypes.CDLL:
     lib.route_fused.restype = ctypes.c_int
     lib.route_topk16_sharded.argtypes = [vp, f32p, i32, i32p, f32p, vp, i32, vp]
     lib.route_topk16_sharded.restype = ctypes.c_int
+    lib.route_packed_weight_bytes.argtypes = [vp]
+    lib.route_packed_weight_bytes.restype = ctypes.c_size_t
+    lib.route_pack_weights.argtypes = [vp, vp, f32p, vp, vp]
+    lib.route_pack_weights.restype = ctypes.c_int
+    lib.route_latent_router_packed.argtypes = [vp, vp, vp, vp, f32p, vp, i32, vp]
+    lib.route_latent_router_packed.restype = ctypes.c_int
+    lib.route_fused_packed.argtypes = [vp, vp, vp, vp, f32p, i32p, f32p, vp, i32, vp]
+    lib.route_fused_packed.restype = ctypes.c_int
     lib.route_destroy.argtypes = [vp]
     lib.route_destroy.restype = None
     lib.route_strerror.argtypes = [ctypes.c_int]
@@ -115,6 +124,7 @@ class Plan:
         self.latent = latent
         self.experts = experts
         self.workspace_bytes = int(LIB.route_workspace_bytes(ctypes.c_void_p(handle)))
+        self.packed_bytes = int(LIB.route_packed_weight_bytes(ctypes.c_void_p(handle)))
 
     def new_workspace(self) -> torch.Tensor:
         """A zero-filled workspace tensor of the size this plan needs."""
@@ -213,3 +223,61 @@ def fused(plan: Plan, x, w_latent, w_router, latent, logits, ids, weights, works
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_fused")
+
+
+def pack_weights(plan: Plan, w_latent, w_router, packed=None, stream=None) -> torch.Tensor:
+    """Reorder both decode weights into the whole-route kernel's consumption
+    order (route_pack_weights); returns the packed uint8 buffer (allocated
+    here if `packed` is None). Whole-route decode plans only."""
+    if packed is None:
+        packed = torch.empty(max(plan.packed_bytes, 16), dtype=torch.uint8,
+                             device=f"cuda:{plan.device}")
+    if packed.dtype != torch.uint8 or packed.numel() < plan.packed_bytes:
+        raise ValueError(f"packed: needs {plan.packed_bytes} uint8 elements")
+    st = LIB.route_pack_weights(
+        ctypes.c_void_p(plan.handle),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent"),
+        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router"),
+        _ptr(packed, torch.uint8, None, "packed"),
+        _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_pack_weights")
+    return packed
+
+
+def _packed_ptr(plan: Plan, packed) -> int:
+    if packed.numel() < plan.packed_bytes:
+        raise ValueError(f"packed: needs {plan.packed_bytes} bytes, has {packed.numel()}")
+    return _ptr(packed, torch.uint8, None, "packed")
+
+
+def latent_router_packed(plan: Plan, x, packed, latent, logits, workspace, rows: int | None = None,
+                         stream=None) -> None:
+    rows = x.shape[0] if rows is None else rows
+    st = LIB.route_latent_router_packed(
+        ctypes.c_void_p(plan.handle),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
+        _packed_ptr(plan, packed),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_latent_router_packed")
+
+
+def fused_packed(plan: Plan, x, packed, latent, logits, ids, weights, workspace,
+                 rows: int | None = None, stream=None) -> None:
+    rows = x.shape[0] if rows is None else rows
+    st = LIB.route_fused_packed(
+        ctypes.c_void_p(plan.handle),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
+        _packed_ptr(plan, packed),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_fused_packed")

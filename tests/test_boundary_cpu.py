@@ -168,4 +168,8 @@ def test_run_calls_reject_null_plan():
     assert route.LIB.route_fused(None, None, None, None, None, None, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_topk16_sharded(None, None, 8, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_workspace_bytes(None) == 0
+    assert route.LIB.route_packed_weight_bytes(None) == 0
+    assert route.LIB.route_pack_weights(None, None, None, None, None) == route.E_ARG
+    assert route.LIB.route_latent_router_packed(None, None, None, None, None, None, 1, None) == route.E_ARG
+    assert route.LIB.route_fused_packed(None, None, None, None, None, None, None, None, 1, None) == route.E_ARG
     route.LIB.route_destroy(None)
