@@ -9,11 +9,13 @@ HBM. Steps are replayed from a HIP graph holding 8 route_fused calls (one per
 weight copy, each on its own input bank); K steps = K/8 replays, timed with
 events on the launch stream between two device synchronisations.
 
-Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows), the
-3072-row prefill chunk, the decode kernel at one tensor-parallel rank's share
-(448 x 112 at 8 ranks, 224 x 56 at 16 ranks; 1, 8 and 20 rows), the decode
-kernel's HBM roofline fraction, the prefill MFMA fraction, and the CPU oracle
-timed on this host (a reported baseline only).
+Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows),
+each also with packed weights (route_fused_packed, the weight copies packed
+once outside the timed region), the 3072-row prefill chunk (packed weights,
+and the [K][N] path beside it), the decode kernel at one tensor-parallel
+rank's share (448 x 112 at 8 ranks, 224 x 56 at 16 ranks; 1, 8 and 20 rows),
+the decode kernel's HBM roofline fraction, the prefill MFMA fraction, and the
+CPU oracle timed on this host (a reported baseline only).
 
 Roofline: a decode route is one kernel launch, so the kernel's average launch
 duration is the event-timed graph replay divided by the launches in it (it
@@ -112,6 +114,22 @@ class DecodeSetup:
 
     def capture(self):
         return capture_graph(self.run_all, self.torch)
+
+
+class PackedDecodeSetup(DecodeSetup):
+    """The same routes through route_fused_packed: each weight copy packed once
+    (route_pack_weights, outside the timed region) into the decode kernel's
+    consumption order."""
+
+    def __init__(self, rows: int, copies, banks_dev, route, torch, packs):
+        super().__init__(rows, copies, banks_dev, route, torch)
+        self.packs = packs
+
+    def run_all(self):
+        r = self.route
+        for i, pk in enumerate(self.packs):
+            r.fused_packed(self.plan, self.xs[i], pk, self.lat[i], self.lg[i], self.ids[i], self.wt[i],
+                           self.ws[i], rows=self.rows)
 
 
 def time_graph(g, replays: int, torch):
@@ -267,24 +285,34 @@ def main():
         return
 
     results = {}
+    packed_results = {}
     widths = [args.rows] + ([int(w) for w in args.widths.split(",") if int(w) != args.rows]
                             if not args.no_extras else [])
     head = None
-    for rows in widths:
-        d = DecodeSetup(rows, copies, banks, route, torch)
-        g = d.capture()
-        reps_w = warm // copies_n
-        for _ in range(reps_w):
-            g.replay()
+    packs = None
+    if not args.no_extras:
+        pplan = route.Plan(route.MODE_DECODE, 20)
+        packs = [route.pack_weights(pplan, w, wr) for w, wr in copies]
         torch.cuda.synchronize()
-        reps = steps // copies_n
-        ms_rep = time_graph(g, reps, torch)
-        us = ms_rep * 1000.0 / copies_n
-        results[rows] = us
-        log(f"decode rows={rows}: {us:.2f} us per route ({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
-        if rows == args.rows:
-            head = (us, ms_rep / copies_n, ms_rep / copies_n)
-        del g, d
+    for rows in widths:
+        variants = [("kn", DecodeSetup(rows, copies, banks, route, torch))]
+        if packs is not None:
+            variants.append(("packed", PackedDecodeSetup(rows, copies, banks, route, torch, packs)))
+        for name, d in variants:
+            g = d.capture()
+            reps_w = warm // copies_n
+            for _ in range(reps_w):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = steps // copies_n
+            ms_rep = time_graph(g, reps, torch)
+            us = ms_rep * 1000.0 / copies_n
+            (results if name == "kn" else packed_results)[rows] = us
+            log(f"decode rows={rows} ({name} weights): {us:.2f} us per route "
+                f"({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
+            if rows == args.rows and name == "kn":
+                head = (us, ms_rep / copies_n, ms_rep / copies_n)
+            del g, d
 
     us8, ms_step, kernel_ms = head
     achieved = decode_bytes(args.rows) / (kernel_ms * 1e-3) / 1e9
@@ -326,21 +354,34 @@ def main():
                 times.append(s.elapsed_time(e) / reps * 1000.0)
             return sorted(times)[1]
 
-        # the whole chunk first (it is the reported figure), then its pieces
-        t_all = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
-        t_lr = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
+        # packed weights (K-contiguous W, router parts split once) first: the
+        # reported figure; then the [K][N] path, which splits the router
+        # weight on every call
+        packed = route.pack_weights(plan, w0, wr0)
+        torch.cuda.synchronize()
+        t_all = t_call(lambda: route.fused_packed(plan, x, packed, lat, lg, ids, wt, ws), args.prefill_reps)
+        t_lr = t_call(lambda: route.latent_router_packed(plan, x, packed, lat, lg, ws), args.prefill_reps)
         t_tk = t_call(lambda: route.topk16(plan, lg, ids, wt), args.prefill_reps)
+        t_all_kn = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
+        t_lr_kn = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
+        del packed
         gemm_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER_MFMA
         prefill = {
-            "rows": rows, "us_per_chunk": round(t_all, 2), "rows_per_s": round(rows / (t_all * 1e-6)),
+            "rows": rows, "weights": "packed (route_pack_weights, once per weight set)",
+            "us_per_chunk": round(t_all, 2), "rows_per_s": round(rows / (t_all * 1e-6)),
             "latent_router_us": round(t_lr, 2), "topk16_us": round(t_tk, 2),
             "mfma_tflops": round(gemm_flops / (t_lr * 1e-6) / 1e12, 1),
             "mfma_frac": round(gemm_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "router_variant": "FP32 weight split into 3 exact BF16 parts, BF16 MFMA, FP32 chains "
                               "restarted every 256 K and folded into FP64",
+            "kn_weights": {"us_per_chunk": round(t_all_kn, 2),
+                           "rows_per_s": round(rows / (t_all_kn * 1e-6)),
+                           "latent_router_us": round(t_lr_kn, 2),
+                           "note": "[K][N] weights; includes the per-call router weight split"},
         }
-        log(f"prefill 3072: {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
-            f"{t_lr:.1f} us = {prefill['mfma_tflops']} TFLOP/s, top-16 {t_tk:.1f} us")
+        log(f"prefill 3072 (packed): {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
+            f"{t_lr:.1f} us = {prefill['mfma_tflops']} TFLOP/s, top-16 {t_tk:.1f} us; [K][N] weights "
+            f"{t_all_kn:.1f} us")
 
     shares = None
     if not args.no_extras:
@@ -380,6 +421,7 @@ def main():
         "decode_us_by_rows": {str(k): round(v, 3) for k, v in sorted(results.items())},
         "decode_hbm_frac_by_rows": {str(k): round(decode_bytes(k) / (v * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
                                     for k, v in sorted(results.items())},
+        "decode_packed_us_by_rows": {str(k): round(v, 3) for k, v in sorted(packed_results.items())},
         "prefill": prefill,
         "rank_share_decode": shares,
     }
