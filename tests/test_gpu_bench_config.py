@@ -3,10 +3,12 @@
 Decode: 8-row route_fused calls captured in one HIP graph over 8 distinct
 weight copies (617 MB of weights, more than the 256 MB Infinity Cache) and
 8 input banks, replayed several times; every output of every copy is checked
-against the oracle on that copy's weights. Prefill: the 3072-row chunk with
-outlier channels that bench.py times, one route_fused call; a seeded sample of
-rows is checked against the oracle row by row (the full chunk is checked in
-the prefill parity tests). Criteria as in the decode and prefill parity tests:
+against the oracle on that copy's weights; the same graph through
+route_fused_packed on the packed copies must give the same bits. Prefill: the
+3072-row chunk with outlier channels that bench.py times, one route_fused
+call and one route_fused_packed call (bitwise equal); a seeded sample of rows
+is checked against the oracle row by row (the full chunk is checked in the
+prefill parity tests). Criteria as in the decode and prefill parity tests:
 latent within 1 BF16 ULP or the cancellation band, relative RMS <= 2.0e-3;
 logits within 2 FP32 ULP; ids equal up to a 1-for-1 swap within 2 FP32 ULP;
 weights within 5 FP32 ULP."""
@@ -67,6 +69,20 @@ def test_decode_graph_over_weight_copies():
                "ids": d.ids[i].cpu().numpy(), "weights": d.wt[i].cpu().numpy()}
         check(got, oracle_rows(xs[i][:8], copy=i), f"copy {i}")
 
+    pplan = route.Plan(route.MODE_DECODE, 20)
+    packs = [route.pack_weights(pplan, w, wr) for w, wr in copies]
+    p = bench.PackedDecodeSetup(8, copies, banks, route, torch, packs)
+    gp = p.capture()
+    for _ in range(3):
+        gp.replay()
+    torch.cuda.synchronize()
+    for i in range(COPIES):
+        assert torch.equal(p.lat[i].view(torch.int16), d.lat[i].view(torch.int16)), i
+        assert torch.equal(p.lg[i].view(torch.int32), d.lg[i].view(torch.int32)), i
+        assert torch.equal(p.ids[i], d.ids[i]), i
+        assert torch.equal(p.wt[i].view(torch.int32), d.wt[i].view(torch.int32)), i
+    log("packed decode graph: bitwise equal on every copy")
+
 
 @pytest.mark.timeout(600)
 def test_prefill_chunk_sampled_rows():
@@ -79,8 +95,16 @@ def test_prefill_chunk_sampled_rows():
     lg = torch.empty((3072, route.EXPERTS), dtype=torch.float32, device="cuda")
     ids = torch.empty((3072, 16), dtype=torch.int32, device="cuda")
     wt = torch.empty((3072, 16), dtype=torch.float32, device="cuda")
-    route.fused(plan, bf16(x), w, wr, lat, lg, ids, wt, ws)
+    xd = bf16(x)
+    packed = route.pack_weights(plan, w, wr)
+    lat_p, lg_p = torch.empty_like(lat), torch.empty_like(lg)
+    ids_p, wt_p = torch.empty_like(ids), torch.empty_like(wt)
+    route.fused_packed(plan, xd, packed, lat_p, lg_p, ids_p, wt_p, ws)
+    route.fused(plan, xd, w, wr, lat, lg, ids, wt, ws)
     torch.cuda.synchronize()
+    assert torch.equal(lat_p.view(torch.int16), lat.view(torch.int16))
+    assert torch.equal(lg_p.view(torch.int32), lg.view(torch.int32))
+    assert torch.equal(ids_p, ids) and torch.equal(wt_p.view(torch.int32), wt.view(torch.int32))
     rows = np.sort(np.random.default_rng(7).choice(3072, 128, replace=False))
     got = {"latent": bits_host(lat)[rows], "logits": lg.cpu().numpy()[rows],
            "ids": ids.cpu().numpy()[rows], "weights": wt.cpu().numpy()[rows]}
