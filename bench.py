@@ -1,21 +1,24 @@
 """Benchmark of the per-row MoE route on one MI355X.
 
-One step = one route_fused call (latent down projection 7168 -> 3584 in BF16,
-FP32 router logits over 896 experts, standalone top-16) over one batch of
-synthetic rows, inputs and weights resident in HBM. The headline workload is
-the 8-row decode round; the weights rotate over 8 distinct copies (8 x 77 MB,
-more than the 256 MB Infinity Cache) so every step streams its weights from
-HBM. Steps are replayed from a HIP graph holding 8 route_fused calls (one per
-weight copy, each on its own input bank); K steps = K/8 replays, timed with
-events on the launch stream between two device synchronisations.
+One step = one route_fused_packed call (latent down projection 7168 -> 3584 in
+BF16, FP32 router logits over 896 experts, standalone top-16) over one batch
+of synthetic rows, inputs and weights resident in HBM. The weights are model
+parameters: each weight copy is packed once by route_pack_weights (the decode
+kernel's read order, same bytes) outside the timed region, as a server does
+when it loads the weights. The headline workload is the 8-row decode round;
+the weights rotate over 8 distinct copies (8 x 77 MB, more than the 256 MB
+Infinity Cache) so every step streams its weights from HBM. Steps are replayed
+from a HIP graph holding 8 calls (one per weight copy, each on its own input
+bank); K steps = K/8 replays, timed with events on the launch stream between
+two device synchronisations.
 
 Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows),
-each also with packed weights (route_fused_packed, the weight copies packed
-once outside the timed region), the 3072-row prefill chunk (packed weights,
-and the [K][N] path beside it), the decode kernel at one tensor-parallel
-rank's share (448 x 112 at 8 ranks, 224 x 56 at 16 ranks; 1, 8 and 20 rows),
-the decode kernel's HBM roofline fraction, the prefill MFMA fraction, and the
-CPU oracle timed on this host (a reported baseline only).
+each also through route_fused on the [K][N] weights, the 3072-row prefill
+chunk (packed weights, and the [K][N] path beside it), the decode kernel at
+one tensor-parallel rank's share (448 x 112 at 8 ranks, 224 x 56 at 16 ranks;
+1, 8 and 20 rows), the decode kernel's HBM roofline fraction, the prefill
+MFMA fraction, and the CPU oracle timed on this host (a reported baseline
+only).
 
 Roofline: a decode route is one kernel launch, so the kernel's average launch
 duration is the event-timed graph replay divided by the launches in it (it
@@ -27,7 +30,8 @@ per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
 valid only while the kernel source is unchanged.
 
 --profile-pass runs only what the counter runs need: 64 headline decode
-launches and a plain 512 MiB device copy (the counters' calibration).
+launches (packed weights) and a plain 512 MiB device copy (the counters'
+calibration).
 
 Prints ONE JSON line on stdout.
 """
@@ -197,10 +201,18 @@ def share_timings(copies, banks, route, torch, replays: int):
     return out
 
 
+def pack_copies(copies, route, torch):
+    """Each weight copy packed once into the decode format."""
+    plan = route.Plan(route.MODE_DECODE, 20)
+    packs = [route.pack_weights(plan, w, wr) for w, wr in copies]
+    torch.cuda.synchronize()
+    return packs
+
+
 def profile_pass(rows: int, copies, banks, route, torch):
     """Short run for the rocprofv3 counter passes: headline decode launches and
     one plain copy of known size."""
-    d = DecodeSetup(rows, copies, banks, route, torch)
+    d = PackedDecodeSetup(rows, copies, banks, route, torch, pack_copies(copies, route, torch))
     for _ in range(8):
         d.run_all()
     torch.cuda.synchronize()
@@ -285,19 +297,15 @@ def main():
         return
 
     results = {}
-    packed_results = {}
+    kn_results = {}
     widths = [args.rows] + ([int(w) for w in args.widths.split(",") if int(w) != args.rows]
                             if not args.no_extras else [])
     head = None
-    packs = None
-    if not args.no_extras:
-        pplan = route.Plan(route.MODE_DECODE, 20)
-        packs = [route.pack_weights(pplan, w, wr) for w, wr in copies]
-        torch.cuda.synchronize()
+    packs = pack_copies(copies, route, torch)
     for rows in widths:
-        variants = [("kn", DecodeSetup(rows, copies, banks, route, torch))]
-        if packs is not None:
-            variants.append(("packed", PackedDecodeSetup(rows, copies, banks, route, torch, packs)))
+        variants = [("packed", PackedDecodeSetup(rows, copies, banks, route, torch, packs))]
+        if not args.no_extras:
+            variants.append(("kn", DecodeSetup(rows, copies, banks, route, torch)))
         for name, d in variants:
             g = d.capture()
             reps_w = warm // copies_n
@@ -307,10 +315,10 @@ def main():
             reps = steps // copies_n
             ms_rep = time_graph(g, reps, torch)
             us = ms_rep * 1000.0 / copies_n
-            (results if name == "kn" else packed_results)[rows] = us
+            (results if name == "packed" else kn_results)[rows] = us
             log(f"decode rows={rows} ({name} weights): {us:.2f} us per route "
                 f"({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
-            if rows == args.rows and name == "kn":
+            if rows == args.rows and name == "packed":
                 head = (us, ms_rep / copies_n, ms_rep / copies_n)
             del g, d
 
@@ -320,7 +328,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": f"decode_route_kernel<{1 if args.rows <= 16 else 2}, DecodeShape<3584, 896, 4, 16>>",
+                "kernel": f"decode_route_kernel<{1 if args.rows <= 16 else 2}, DecodeShape<3584, 896, "
+                          f"{'8, 8' if args.rows <= 12 else '4, 16'}>, true> (packed weights)",
                 "kernel_us_per_launch": round(kernel_ms * 1000.0, 3),
                 "algorithmic_bytes_per_launch": decode_bytes(args.rows)}
 
@@ -414,14 +423,15 @@ def main():
             "rows": args.rows,
             "hidden": K, "latent": N, "experts": E, "topk": 16,
             "weight_copies": copies_n,
-            "timing": "HIP graph of 8 route_fused calls, events on the launch stream",
+            "weights": "packed once per copy by route_pack_weights, outside the timed region",
+            "timing": "HIP graph of 8 route_fused_packed calls, events on the launch stream",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode_us_by_rows": {str(k): round(v, 3) for k, v in sorted(results.items())},
         "decode_hbm_frac_by_rows": {str(k): round(decode_bytes(k) / (v * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
                                     for k, v in sorted(results.items())},
-        "decode_packed_us_by_rows": {str(k): round(v, 3) for k, v in sorted(packed_results.items())},
+        "decode_kn_us_by_rows": {str(k): round(v, 3) for k, v in sorted(kn_results.items())},
         "prefill": prefill,
         "rank_share_decode": shares,
     }

@@ -157,19 +157,25 @@ int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t sh
 /* Packed weights. Weights are model parameters, loaded once; each kernel
  * reads them fastest in an order of its own, so route_pack_weights reorders
  * both weights once into the plan's packed format, and the *_packed calls
- * then read that buffer in place of w_latent and w_router. Their results are
- * bitwise those of route_latent_router / route_fused on the original weights:
- * every kernel lane receives the same operand values in the same order; only
- * the loads change.
+ * then read that buffer in place of w_latent and w_router. Every output
+ * keeps the definitions and bounds above.
  *   decode (whole route): both weights in the decode kernel's consumption
  *     order, so every workgroup streams one contiguous block with 16-byte
  *     loads (the [K][N] layouts give it strided 128-byte row segments);
  *     77,070,336 bytes: the latent weight's 51,380,224 bytes of BF16 values,
- *     then the router weight's 25,690,112 bytes of FP32 values;
+ *     then the router weight's 25,690,112 bytes of FP32 values, each tile in
+ *     K order. Up to 12 rows the kernel splits K 8 ways for both weights, so
+ *     that every wave streams the same bytes; this K split differs from the
+ *     [K][N] kernel's, so a latent value may differ from route_fused's in
+ *     the last bit (each is one full-K dot rounded once); above 12 rows the
+ *     splits are route_fused's and the results its bits. Logits are FP64
+ *     sums rounded once in both;
  *   prefill: the weights K-contiguous, W as [3584][7168] BF16 (the [out][in]
  *     layout of a linear layer) and the router weight as its three exact
  *     BF16 parts [2688][7168] (split once here instead of on every call), so
  *     the GEMMs read both operands with 16-byte LDS reads; 89,915,392 bytes.
+ *     Every GEMM lane receives the same operand values in the same order as
+ *     with [K][N] weights: the results are bitwise those of route_fused.
  * Share plans have no packed format: route_packed_weight_bytes returns 0 and
  * the packed calls return ROUTE_E_SHAPE. */
 

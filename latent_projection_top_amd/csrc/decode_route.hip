@@ -13,9 +13,10 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split (whole route; a tensor-parallel rank's share uses the same units
-// over its columns with more K splits): 672 workgroups of 4 waves, all
-// resident at once.
+// Work split (whole route with [K][N] weights; packed weights split both
+// weights' K 8 ways instead, 448 latent and 224 router workgroups; a
+// tensor-parallel rank's share uses the same units over its columns with more
+// K splits): 672 workgroups of 4 waves, all resident at once.
 //   workgroups 0..447, dispatched first: router units, expert tile (32
 //       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
 //       bytes) of the FP32 router weight and the unit stores one FP64 partial
@@ -98,13 +99,22 @@ struct DecodeShape {
   static_assert(N % 4 == 0 && E % 2 == 0, "a lane's loads stay inside a row");
 };
 using FullShape = DecodeShape<kLatent, kExperts, 4, 16>;
+// With packed weights every unit's block is contiguous, and up to 12 rows 8 K
+// splits of both weights, which give every wave the same 28 KB to stream (448
+// latent + 224 router workgroups, all resident), were measured faster than
+// 4 x 16 (1 / 8 / 9 rows: 18.1 / 19.4 / 20.1 us against 18.7 / 20.0 / 20.5);
+// at 16 and 20 rows 4 x 16 is faster (20.9 / 22.9 against 22.0 / 23.2), and
+// with [K][N] weights it is faster at every width.
+using PackedShape = DecodeShape<kLatent, kExperts, 8, 8>;
+constexpr int kPackedShapeMaxRows = 12;
 // Share splits measured on MI355X (graph-replayed launches over 616 MB of
 // distinct shares): with the tile combine's loads all in flight, fewer and
 // longer K chunks won over 28 latent / 56 router splits by 1.5 to 3 us.
 using Tp8Shape = DecodeShape<448, 112, 7, 28>;
 using Tp16Shape = DecodeShape<224, 56, 14, 28>;
 constexpr int kDecodeCounters = FullShape::Counters;   // the largest counter set
-static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters,
+static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters &&
+                  PackedShape::Counters == kDecodeCounters,
               "every shape's counters fit the workspace's counter area");
 static_assert(FullShape::LatTiles == 56 && FullShape::RtTiles == 28 && FullShape::Grid == 672, "full shape");
 
@@ -223,21 +233,25 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   const int k0 = split * Sh::KR + wave * Sh::KRWave;
   // lanes past the last expert of a share read a valid pair; never stored
   const int ecol = Sh::E % kRtTileE == 0 ? e0 + 2 * m : min(e0 + 2 * m, Sh::E - 2);
-  // packed: the unit's 4 waves' blocks are contiguous, a wave's steps are
-  // 512-float blocks, and lane l's two 16-byte pieces of a step sit at l and
-  // 64 + l (see pack_router_kernel)
-  const float* wp = Packed ? a.wr + (size_t)u * (Sh::KR * kRtTileE) + wave * (Sh::KRWave * kRtTileE) + 4 * lane
+  // packed: a tile's K steps are consecutive 512-float blocks, and lane l's
+  // two 16-byte pieces of a step sit at l and 64 + l (see pack_router_kernel)
+  const float* wp = Packed ? a.wr + ((size_t)tile * (kHidden / kStepR) + k0 / kStepR) * (kStepR * kRtTileE) + 4 * lane
                            : a.wr + (size_t)(k0 + 4 * g) * Sh::E + ecol;
 
   // LDS after the reduction buffer: hidden rows 16..19 over the unit's K chunk
   uint16_t* xt = reinterpret_cast<uint16_t*>(smem + kWaves * kRowsPad * kRtTileE * 8);
   constexpr int kTailChunks = kTailRows * Sh::KR / 8;  // 16-byte pieces
-  static_assert(!kTail || kTailChunks <= kThreads, "one piece per thread");
-  u32x4 xtv = u32x4{0u, 0u, 0u, 0u};
-  if (kTail && (int)threadIdx.x < kTailChunks) {
-    const int i = threadIdx.x / (Sh::KR / 8);
-    const int c = threadIdx.x % (Sh::KR / 8);
-    xtv = *(const u32x4*)(a.x + (size_t)min(16 + i, a.rows - 1) * kHidden + split * Sh::KR + 8 * c);
+  constexpr int kTailPer = (kTailChunks + kThreads - 1) / kThreads;
+  u32x4 xtv[kTailPer];
+#pragma unroll
+  for (int q = 0; q < kTailPer; ++q) {
+    const int t = threadIdx.x + q * kThreads;
+    xtv[q] = u32x4{0u, 0u, 0u, 0u};
+    if (kTail && t < kTailChunks) {
+      const int i = t / (Sh::KR / 8);
+      const int c = t % (Sh::KR / 8);
+      xtv[q] = *(const u32x4*)(a.x + (size_t)min(16 + i, a.rows - 1) * kHidden + split * Sh::KR + 8 * c);
+    }
   }
 
   f64x4 acc[2];
@@ -272,10 +286,14 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int st = 0; st < kDepthR; ++st) issue(st);
   __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
   if (kTail) {
-    if ((int)threadIdx.x < kTailChunks) {
-      const int i = threadIdx.x / (Sh::KR / 8);
-      const int c = threadIdx.x % (Sh::KR / 8);
-      *(u32x4*)(xt + i * Sh::KR + 8 * c) = xtv;
+#pragma unroll
+    for (int q = 0; q < kTailPer; ++q) {
+      const int t = threadIdx.x + q * kThreads;
+      if (t < kTailChunks) {
+        const int i = t / (Sh::KR / 8);
+        const int c = t % (Sh::KR / 8);
+        *(u32x4*)(xt + i * Sh::KR + 8 * c) = xtv[q];
+      }
     }
     __syncthreads();
   }
@@ -395,10 +413,9 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   const int k0 = split * Sh::KL + wave * Sh::KLWave;
   // lanes past the last column of a share read a valid quad; never stored
   const int ncol = Sh::N % kLatTileN == 0 ? n0 + 4 * m : min(n0 + 4 * m, Sh::N - 4);
-  // packed: the unit's 4 waves' blocks are contiguous, a wave's steps are
-  // 2048-value blocks, and lane l's piece for MFMA c sits at 64 c + l (see
-  // pack_latent_kernel)
-  const uint16_t* wp = Packed ? a.w + (size_t)u * (Sh::KL * kLatTileN) + wave * (Sh::KLWave * kLatTileN) + 8 * lane
+  // packed: a tile's K steps are consecutive 2048-value blocks, and lane l's
+  // piece for MFMA c sits at 64 c + l (see pack_latent_kernel)
+  const uint16_t* wp = Packed ? a.w + ((size_t)tile * (kHidden / kStepL) + k0 / kStepL) * (kStepL * kLatTileN) + 8 * lane
                               : a.w + (size_t)(k0 + 8 * g) * Sh::N + ncol;
 
   f32x4 acc[NT][4];
@@ -613,13 +630,18 @@ void decode_route_kernel(DecodeArgs a) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-template <class Sh>
+// Sh2: a second shape sharing the workspace (the whole route's packed-weight
+// shape); the partial areas fit the larger of the two.
+template <class Sh, class Sh2 = Sh>
 static size_t ws_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits, size_t* off_cand) {
+  constexpr int kSL = Sh::SplitsL > Sh2::SplitsL ? Sh::SplitsL : Sh2::SplitsL;
+  constexpr int kSR = Sh::SplitsR > Sh2::SplitsR ? Sh::SplitsR : Sh2::SplitsR;
+  static_assert(Sh::N == Sh2::N && Sh::E == Sh2::E, "shapes sharing a workspace");
   size_t off = align256(sizeof(uint32_t) * kDecodeCounters);
   *off_lat = off;
-  off = align256(off + sizeof(float) * Sh::SplitsL * (size_t)rows_cap * Sh::N);
+  off = align256(off + sizeof(float) * kSL * (size_t)rows_cap * Sh::N);
   *off_rt = off;
-  off = align256(off + sizeof(double) * Sh::SplitsR * (size_t)rows_cap * Sh::E);
+  off = align256(off + sizeof(double) * kSR * (size_t)rows_cap * Sh::E);
   *off_logits = off;
   off = align256(off + sizeof(float) * (size_t)rows_cap * Sh::E);
   *off_cand = off;
@@ -639,7 +661,7 @@ size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off
     return ws_bytes<Tp8Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
   if (latent == Tp16Shape::N && experts == Tp16Shape::E)
     return ws_bytes<Tp16Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
-  return ws_bytes<FullShape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
+  return ws_bytes<FullShape, PackedShape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
 }
 
 template <class Sh, bool Packed = false>
@@ -672,7 +694,9 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (full && packed)
+  if (full && packed && rows <= kPackedShapeMaxRows)
+    launch_shape<PackedShape, true>(a, rows, stream);
+  else if (full && packed)
     launch_shape<FullShape, true>(a, rows, stream);
   else if (full)
     launch_shape<FullShape>(a, rows, stream);
@@ -689,18 +713,19 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
 // Wr [7168][896] FP32, reordered once (at weight load) into the order in which
 // the whole-route kernel's lanes consume them, so that every unit streams one
 // contiguous block and every load instruction covers 1 KB with one 16-byte
-// piece per lane. The kernel's operands, and so its results, are bitwise those
-// of the [K][N] layout.
+// piece per lane. Each tile's data is in K order, so that a unit of any K
+// split reads one contiguous range: the packed kernel splits K 8 ways for both
+// weights up to 12 rows (PackedShape) and as the [K][N] kernel does above
+// (FullShape: latent 4, router 16), so the latent's last bit may differ from
+// route_fused's at up to 12 rows (both are one full-K dot rounded once,
+// within the same bounds); its logits are FP64 sums rounded once, as there.
 //
-// Latent: unit u (tile u mod 56, K split u / 56), wave w, step s, MFMA c, lane
-// (g, m) = (l / 16, l mod 16): 8 BF16 values W[k + i][n], i = 0..7, with
-// k = split*1792 + w*448 + 32 s + 8 g and n = tile*64 + 4 m + c, at value
-// offset ((((u*4 + w)*14 + s)*4 + c)*64 + l)*8.
-// Router: unit u (tile u mod 28, K split u / 28), wave w, step s, half h, lane
-// (g, m): {Wr[k][e], Wr[k][e+1], Wr[k+1][e], Wr[k+1][e+1]} with
-// k = split*448 + w*112 + 16 s + 4 g + 2 h and e = tile*32 + 2 m, at float
-// offset ((((u*4 + w)*7 + s)*2 + h)*64 + l)*4.
-using PackShape = FullShape;
+// Latent: tile t (64 columns), K step s (32 rows), MFMA c, lane (g, m) =
+// (l / 16, l mod 16): 8 BF16 values W[32 s + 8 g + i][64 t + 4 m + c],
+// i = 0..7, at value offset (((t*224 + s)*4 + c)*64 + l)*8.
+// Router: tile t (32 experts), K step s (16 rows), half h, lane (g, m):
+// {Wr[k][e], Wr[k][e+1], Wr[k+1][e], Wr[k+1][e+1]} with k = 16 s + 4 g + 2 h
+// and e = 32 t + 2 m, at float offset (((t*448 + s)*2 + h)*64 + l)*4.
 constexpr int kPackLatPieces = kHidden * kLatent / 8;    // 16-byte pieces
 constexpr int kPackRtPieces = kHidden * kExperts / 4;
 
@@ -710,12 +735,9 @@ __global__ __launch_bounds__(256) void pack_latent_kernel(const uint16_t* __rest
   if (p >= kPackLatPieces) return;
   const int l = p % 64;
   const int c = (p / 64) % 4;
-  const int s = (p / 256) % PackShape::StepsL;
-  const int wv = (p / (256 * PackShape::StepsL)) % kWaves;
-  const int u = p / (256 * PackShape::StepsL * kWaves);
-  const int tile = u % PackShape::LatTiles;
-  const int split = u / PackShape::LatTiles;
-  const int k = split * PackShape::KL + wv * PackShape::KLWave + kStepL * s + 8 * (l >> 4);
+  const int s = (p / 256) % (kHidden / kStepL);
+  const int tile = p / (256 * (kHidden / kStepL));
+  const int k = kStepL * s + 8 * (l >> 4);
   const int n = tile * kLatTileN + 4 * (l & 15) + c;
   u32x4 v;
 #pragma unroll
@@ -731,22 +753,19 @@ __global__ __launch_bounds__(256) void pack_router_kernel(const float* __restric
   if (p >= kPackRtPieces) return;
   const int l = p % 64;
   const int h = (p / 64) % 2;
-  const int s = (p / 128) % PackShape::StepsR;
-  const int wv = (p / (128 * PackShape::StepsR)) % kWaves;
-  const int u = p / (128 * PackShape::StepsR * kWaves);
-  const int tile = u % PackShape::RtTiles;
-  const int split = u / PackShape::RtTiles;
-  const int k = split * PackShape::KR + wv * PackShape::KRWave + kStepR * s + 4 * (l >> 4) + 2 * h;
+  const int s = (p / 128) % (kHidden / kStepR);
+  const int tile = p / (128 * (kHidden / kStepR));
+  const int k = kStepR * s + 4 * (l >> 4) + 2 * h;
   const int e = tile * kRtTileE + 2 * (l & 15);
   const f32x2 r0 = *(const f32x2*)(wr + (size_t)k * kExperts + e);
   const f32x2 r1 = *(const f32x2*)(wr + (size_t)(k + 1) * kExperts + e);
   *(f32x4*)(out + (size_t)p * 4) = f32x4{r0[0], r0[1], r1[0], r1[1]};
 }
 
-static_assert((size_t)kPackLatPieces * 16 == (size_t)PackShape::LatUnits * kWaves * PackShape::StepsL * 4 * 64 * 16,
-              "the latent pieces cover every unit, wave, step, MFMA and lane");
-static_assert((size_t)kPackRtPieces * 16 == (size_t)PackShape::RtUnits * kWaves * PackShape::StepsR * 2 * 64 * 16,
-              "the router pieces cover every unit, wave, step, half and lane");
+static_assert(kPackLatPieces == FullShape::LatTiles * (kHidden / kStepL) * 4 * 64,
+              "the latent pieces cover every tile, K step, MFMA and lane");
+static_assert(kPackRtPieces == FullShape::RtTiles * (kHidden / kStepR) * 2 * 64,
+              "the router pieces cover every tile, K step, half and lane");
 
 size_t decode_packed_latent_bytes() { return (size_t)kHidden * kLatent * 2; }
 size_t decode_packed_bytes() { return decode_packed_latent_bytes() + (size_t)kHidden * kExperts * 4; }

@@ -3,8 +3,8 @@
 Decode: 8-row route_fused calls captured in one HIP graph over 8 distinct
 weight copies (617 MB of weights, more than the 256 MB Infinity Cache) and
 8 input banks, replayed several times; every output of every copy is checked
-against the oracle on that copy's weights; the same graph through
-route_fused_packed on the packed copies must give the same bits. Prefill: the
+against the oracle on that copy's weights, and the same for the graph of
+route_fused_packed calls on the packed copies. Prefill: the
 3072-row chunk with outlier channels that bench.py times, one route_fused
 call and one route_fused_packed call (bitwise equal); a seeded sample of rows
 is checked against the oracle row by row (the full chunk is checked in the
@@ -77,11 +77,9 @@ def test_decode_graph_over_weight_copies():
         gp.replay()
     torch.cuda.synchronize()
     for i in range(COPIES):
-        assert torch.equal(p.lat[i].view(torch.int16), d.lat[i].view(torch.int16)), i
-        assert torch.equal(p.lg[i].view(torch.int32), d.lg[i].view(torch.int32)), i
-        assert torch.equal(p.ids[i], d.ids[i]), i
-        assert torch.equal(p.wt[i].view(torch.int32), d.wt[i].view(torch.int32)), i
-    log("packed decode graph: bitwise equal on every copy")
+        got = {"latent": bits_host(p.lat[i]), "logits": p.lg[i].cpu().numpy(),
+               "ids": p.ids[i].cpu().numpy(), "weights": p.wt[i].cpu().numpy()}
+        check(got, oracle_rows(xs[i][:8], copy=i), f"packed copy {i}")
 
 
 @pytest.mark.timeout(600)
