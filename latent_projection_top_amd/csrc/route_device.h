@@ -336,27 +336,18 @@ __device__ __forceinline__ void write_selection(uint64_t k, int32_t* __restrict_
 // One wave selects the 16 largest of a row's 896 logits and writes ids (in
 // selection order) and normalised sigmoid weights. Lane l owns experts l,
 // l + 64, ..., l + 832 as distinct 64-bit keys.
-template <bool Coherent = false, class AfterLoads>
+template <bool Coherent = false>
 __device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32_t* __restrict__ ids,
-                                            float* __restrict__ weights, uint64_t* scratch,
-                                            AfterLoads after_loads) {
+                                            float* __restrict__ weights, uint64_t* scratch) {
   const int lane = threadIdx.x & (kWave - 1);
   float v[14];
 #pragma unroll
   for (int i = 0; i < 14; ++i) v[i] = load_logit<Coherent>(row + i * kWave + lane);
-  // (runs after the loads are issued and before any is waited for)
-  after_loads();
   uint64_t c[14];
 #pragma unroll
   for (int i = 0; i < 14; ++i)
     c[i] = ((uint64_t)logit_key(v[i]) << 32) | (uint64_t)(~(uint32_t)(i * kWave + lane));
   write_selection(select16<14>(c, scratch), ids, weights);
-}
-
-template <bool Coherent = false>
-__device__ __forceinline__ void topk16_wave(const float* __restrict__ row, int32_t* __restrict__ ids,
-                                            float* __restrict__ weights, uint64_t* scratch) {
-  topk16_wave<Coherent>(row, ids, weights, scratch, [] {});
 }
 
 }  // namespace route
