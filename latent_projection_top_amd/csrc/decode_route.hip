@@ -107,6 +107,19 @@ using FullShape = DecodeShape<kLatent, kExperts, 4, 16>;
 // with [K][N] weights it is faster at every width.
 using PackedShape = DecodeShape<kLatent, kExperts, 8, 8>;
 constexpr int kPackedShapeMaxRows = 12;
+
+// Latent units of the packed 8 x 8 launch hold their stream back for 2.6 us
+// (260 ticks of the 100 MHz realtime counter) after they start, so that the
+// router's stream, which feeds the longer chain of dependent steps (tile
+// combine, router completion, top-16), has the memory to itself first; the
+// latent units, whose chain after the stream is shorter, still end in time.
+// Measured (graph over 8 weight copies): 1 / 2 / 4 / 8 / 9 rows 17.2 / 17.5 /
+// 18.1 / 19.0 / 19.45 us against 18.2 / 18.6 / 18.9 / 19.15 / 19.6 without
+// the hold; 2.0 and 3.2 us holds were slower than 2.6. With 4 x 16 splits
+// (16 router splits: the router stream already ends first) a hold did not
+// help. A bounded wait on a clock, not on another workgroup.
+template <class Sh>
+constexpr uint64_t latent_hold_ticks() { return Sh::SplitsL == 8 && Sh::SplitsR == 8 ? 260 : 0; }
 // Share splits measured on MI355X (graph-replayed launches over 616 MB of
 // distinct shares): with the tile combine's loads all in flight, fewer and
 // longer K chunks won over 28 latent / 56 router splits by 1.5 to 3 us.
@@ -423,6 +436,10 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (Packed && latent_hold_ticks<Sh>() > 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < latent_hold_ticks<Sh>()) __builtin_amdgcn_s_sleep(2);
+  }
   constexpr int kDepth = depth<NT>() < Sh::StepsL ? depth<NT>() : Sh::StepsL;
   u32x2 wv[kDepth][8];
   u32x4 wq[kDepth][4];
