@@ -204,3 +204,67 @@ def test_share_graph_replay(ranks):
     torch.cuda.synchronize()
     assert bad == 0
     assert int(ws[:512].count_nonzero()) == 0
+
+
+@pytest.mark.timeout(600)
+def test_packed_graph_replay_mixed_widths_one_workspace():
+    """route_fused_packed at 1, 8, 13 and 20 rows (both packed launch shapes)
+    on one workspace, captured in one HIP graph with the outputs poisoned
+    inside it; every replay takes new banks and must equal the eager calls."""
+    widths = (1, 8, 13, 20)
+    replays = 500
+    log(f"packed graph replay stress widths={widths} replays={replays}")
+    w, wr = weights_dev(0)
+    plan = route.Plan(route.MODE_DECODE, 20)
+    packed = route.pack_weights(plan, w, wr)
+    ws = plan.new_workspace()
+    nb = 16
+    banks = [bf16_dev(gen.hidden(20, bank=21000 + b)) for b in range(nb)]
+    refs = []
+    for b in range(nb):
+        per = []
+        for width in widths:
+            o = Outputs(width)
+            route.fused_packed(plan, banks[b][:width], packed, o.latent, o.logits, o.ids, o.weights,
+                               ws, rows=width)
+            per.append(o)
+        refs.append(per)
+    torch.cuda.synchronize()
+    assert decode_counters_idle(ws)
+
+    x_static = torch.empty_like(banks[0])
+    x_static.copy_(banks[0])
+    outs = [Outputs(width) for width in widths]
+
+    def run():
+        for width, o in zip(widths, outs):
+            o.poison()
+            route.fused_packed(plan, x_static[:width], packed, o.latent, o.logits, o.ids, o.weights,
+                               ws, rows=width)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+
+    mismatches = 0
+    for i in range(replays):
+        b = (i * 5 + 1) % nb
+        x_static.copy_(banks[b])
+        g.replay()
+        for o, r in zip(outs, refs[b]):
+            same = (torch.equal(o.latent, r.latent) and torch.equal(o.logits, r.logits)
+                    and torch.equal(o.ids, r.ids)
+                    and torch.equal(o.weights.view(torch.int32), r.weights.view(torch.int32)))
+            mismatches += 0 if same else 1
+        if i % 100 == 0:
+            log(f"  replay {i}: mismatches so far {mismatches}")
+    torch.cuda.synchronize()
+    assert mismatches == 0
+    assert decode_counters_idle(ws)
