@@ -13,10 +13,11 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split (whole route with [K][N] weights; packed weights split both
-// weights' K 8 ways instead, 448 latent and 224 router workgroups; a
-// tensor-parallel rank's share uses the same units over its columns with more
-// K splits): 672 workgroups of 4 waves, all resident at once.
+// Work split (whole route with [K][N] weights, and packed weights above 12
+// rows; up to 12 rows packed weights split both weights' K 8 ways instead,
+// 224 router then 448 latent workgroups, see PackedShape; a tensor-parallel
+// rank's share uses the same units over its columns with more K splits): 672
+// workgroups of 4 waves, all resident at once.
 //   workgroups 0..447, dispatched first: router units, expert tile (32
 //       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
 //       bytes) of the FP32 router weight and the unit stores one FP64 partial
@@ -643,8 +644,9 @@ void decode_route_kernel(DecodeArgs a) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Sh2: a second shape sharing the workspace (the whole route's packed-weight
-// shape); the partial areas fit the larger of the two.
+// Sh2: a second shape sharing the workspace (the whole route's 8 x 8 packed
+// launch shares the [K][N] launch's counters and partial areas); each partial
+// area fits the larger of the two.
 template <class Sh, class Sh2 = Sh>
 static size_t ws_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits, size_t* off_cand) {
   constexpr int kSL = Sh::SplitsL > Sh2::SplitsL ? Sh::SplitsL : Sh2::SplitsL;
