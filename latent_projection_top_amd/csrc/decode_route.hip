@@ -13,11 +13,11 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split (whole route with [K][N] weights, and packed weights above 12
-// rows; up to 12 rows packed weights split both weights' K 8 ways instead,
-// 224 router then 448 latent workgroups, see PackedShape; a tensor-parallel
-// rank's share uses the same units over its columns with more K splits): 672
-// workgroups of 4 waves, all resident at once.
+// Work split (whole route with [K][N] weights; packed weights split both
+// weights' K 8 ways instead, 224 router then 448 latent workgroups, see
+// PackedShape; a tensor-parallel rank's share uses the same units over its
+// columns with more K splits): 672 workgroups of 4 waves, all resident at
+// once.
 //   workgroups 0..447, dispatched first: router units, expert tile (32
 //       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
 //       bytes) of the FP32 router weight and the unit stores one FP64 partial
@@ -100,14 +100,14 @@ struct DecodeShape {
   static_assert(N % 4 == 0 && E % 2 == 0, "a lane's loads stay inside a row");
 };
 using FullShape = DecodeShape<kLatent, kExperts, 4, 16>;
-// With packed weights every unit's block is contiguous, and up to 12 rows 8 K
-// splits of both weights, which give every wave the same 28 KB to stream (448
-// latent + 224 router workgroups, all resident), were measured faster than
-// 4 x 16 (1 / 8 / 9 rows: 18.1 / 19.4 / 20.1 us against 18.7 / 20.0 / 20.5);
-// at 16 and 20 rows 4 x 16 is faster (20.9 / 22.9 against 22.0 / 23.2), and
-// with [K][N] weights it is faster at every width.
+// With packed weights every unit's block is contiguous, and 8 K splits of
+// both weights, which give every wave the same 28 KB to stream (224 router +
+// 448 latent workgroups, all resident), with the latent hold and the router
+// prefetch depth below, were measured faster than 4 x 16 at every width (1 /
+// 8 / 12 / 16 / 20 rows: 17.5 / 18.7 / 19.5 / 20.3 / 21.8 us against 18.7 /
+// 20.0 / 20.9 / 20.9 / 22.9); with [K][N] weights 4 x 16 is faster at every
+// width.
 using PackedShape = DecodeShape<kLatent, kExperts, 8, 8>;
-constexpr int kPackedShapeMaxRows = 12;
 
 // Latent units of the packed 8 x 8 launch hold their stream back for 2.6 us
 // (260 ticks of the 100 MHz realtime counter) after they start, so that the
@@ -121,6 +121,17 @@ constexpr int kPackedShapeMaxRows = 12;
 // help. A bounded wait on a clock, not on another workgroup.
 template <class Sh>
 constexpr uint64_t latent_hold_ticks() { return Sh::SplitsL == 8 && Sh::SplitsR == 8 ? 260 : 0; }
+
+// Router steps of loads kept in flight per wave. The 8 x 8 launch's router
+// waves have 14 steps and, while the latent units hold, the memory to
+// themselves: all 14 in flight up to 16 rows (8 / 12 rows 0.3 us faster than
+// 7), 10 at 17..20 rows (14 spill registers there). Otherwise up to 7 (all of
+// a 4 x 16 router wave's).
+template <int NT, class Sh>
+constexpr int router_depth() {
+  const int d = (Sh::SplitsL == 8 && Sh::SplitsR == 8) ? (NT == 1 ? 14 : 10) : 7;
+  return Sh::StepsR < d ? Sh::StepsR : d;
+}
 // Share splits measured on MI355X (graph-replayed launches over 616 MB of
 // distinct shares): with the tile combine's loads all in flight, fewer and
 // longer K chunks won over 28 latent / 56 router splits by 1.5 to 3 us.
@@ -274,7 +285,7 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
   double tacc[kTailRows][2];
 #pragma unroll
   for (int i = 0; i < kTailRows; ++i) tacc[i][0] = tacc[i][1] = 0.0;
-  constexpr int kDepthR = Sh::StepsR < 7 ? Sh::StepsR : 7;
+  constexpr int kDepthR = router_depth<NT, Sh>();
   f32x2 wv[kDepthR][4];
   u32x2 xv[kDepthR];
   auto issue = [&](int st) {
@@ -293,9 +304,9 @@ __device__ bool router_unit(const DecodeArgs& a, const int u, char* smem, int* s
     }
     xv[st % kDepthR] = *(const u32x2*)(a.x + (size_t)xr[0] * kHidden + k0 + 4 * g + st * kStepR);
   };
-  // up to 7 steps of loads in flight: all of them for the whole route
+  // router_depth() steps of loads in flight: all 7 of a 4 x 16 router wave's
   // (measured: 0.3 us faster at 8 rows and 0.5 us at 20 rows than 4 steps
-  // ahead, at the same register count)
+  // ahead, at the same register count), 14 or 10 of an 8 x 8 wave's
 #pragma unroll
   for (int st = 0; st < kDepthR; ++st) issue(st);
   __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
@@ -709,10 +720,8 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (full && packed && rows <= kPackedShapeMaxRows)
+  if (full && packed)
     launch_shape<PackedShape, true>(a, rows, stream);
-  else if (full && packed)
-    launch_shape<FullShape, true>(a, rows, stream);
   else if (full)
     launch_shape<FullShape>(a, rows, stream);
   else if (n_latent == Tp8Shape::N)
@@ -729,11 +738,11 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
 // the whole-route kernel's lanes consume them, so that every unit streams one
 // contiguous block and every load instruction covers 1 KB with one 16-byte
 // piece per lane. Each tile's data is in K order, so that a unit of any K
-// split reads one contiguous range: the packed kernel splits K 8 ways for both
-// weights up to 12 rows (PackedShape) and as the [K][N] kernel does above
-// (FullShape: latent 4, router 16), so the latent's last bit may differ from
-// route_fused's at up to 12 rows (both are one full-K dot rounded once,
-// within the same bounds); its logits are FP64 sums rounded once, as there.
+// split reads one contiguous range. The packed kernel splits K 8 ways for both
+// weights (PackedShape) where the [K][N] kernel splits the latent 4 and the
+// router 16 ways, so the latent's last bit may differ from route_fused's
+// (both are one full-K dot rounded once, within the same bounds); its logits
+// are FP64 sums rounded once, as there.
 //
 // Latent: tile t (64 columns), K step s (32 rows), MFMA c, lane (g, m) =
 // (l / 16, l mod 16): 8 BF16 values W[32 s + 8 g + i][64 t + 4 m + c],
