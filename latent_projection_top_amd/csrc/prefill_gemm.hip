@@ -207,22 +207,23 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   const char* b_src = reinterpret_cast<const char*>(w);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-  auto issue = [&](int kt) {
+  auto issue_one = [&](int kt, int i) {
     const uint32_t st = lds0 + (kt % kGStages) * S::STAGE;
     const char* ab = a_src + (size_t)kt * (kGBK * 2);
     const char* bb = b_src + (BT ? (size_t)kt * (kGBK * 2) : (size_t)kt * ((size_t)kGBK * S::N * 2));
-#pragma unroll
-    for (int i = 0; i < S::PER_WAVE; ++i) {
-      const int c = wave + kGWaves * i;
-      if (i < kAW)
-        dma16(ab, off[i], st + c * 1024);
-      else if (c < S::LOADS) {
-        if constexpr (BT)
-          dma16(bb + (size_t)(i - kAW) * kBtStep, off[kAW], st + c * 1024);
-        else
-          dma16(bb, off[i], st + c * 1024);
-      }
+    const int c = wave + kGWaves * i;
+    if (i < kAW)
+      dma16(ab, off[i], st + c * 1024);
+    else if (c < S::LOADS) {
+      if constexpr (BT)
+        dma16(bb + (size_t)(i - kAW) * kBtStep, off[kAW], st + c * 1024);
+      else
+        dma16(bb, off[i], st + c * 1024);
     }
+  };
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < S::PER_WAVE; ++i) issue_one(kt, i);
   };
 
   // ---- LDS -> register operand addresses ----------------------------------
@@ -292,11 +293,18 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   // with the next K half's value as soon as its last MFMA has been issued
   // (a[i] after row i, b[j] in the last row), so the next half's operands
   // arrive while this half's MFMAs run, without a second register set.
-  auto step = [&](Ops& o, bool restart, bool reload, uint32_t st_n, int s_n) {
+  auto step = [&](Ops& o, bool restart, bool reload, uint32_t st_n, int s_n, int dma_kt) {
 #pragma unroll
     for (int i = 0; i < S::MT; ++i) {
 #pragma unroll
       for (int j = 0; j < S::NT; ++j) {
+        {
+          // spread this wave's loads of stage dma_kt over the MFMAs: load d
+          // goes out after MFMA kEvery * d + 1
+          constexpr int kEvery = (S::MT * S::NT) / S::PER_WAVE;
+          const int p = i * S::NT + j;
+          if (dma_kt >= 0 && p % kEvery == 1 && p / kEvery < S::PER_WAVE) issue_one(dma_kt, p / kEvery);
+        }
         if constexpr (Router) {
           const int c = j < 2 ? j : 2 + (j & 1);
           const bool z = restart && j < 4;  // first MFMA of each chain in the period
@@ -334,13 +342,18 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
 #pragma unroll
     for (int u = 0; u < kGFoldStages; ++u) {
       const int kt = kp + u;
-      step(o, u == 0, true, stage_lds(kt), 1);
+      step(o, u == 0, true, stage_lds(kt), 1, -1);
       lgkm_wait0();
       vm_wait_stages<S::PER_WAVE>(full_wave, kt + 2 < kGKT ? 1 : 0);
       __syncthreads();
-      if (kt + 3 < kGKT) issue(kt + 3);
       // (after the last stage this reads a stale buffer; the values go unused)
-      step(o, false, true, stage_lds(kt + 1), 0);
+      // Stage kt + 3's loads: the router GEMM spreads them over the second
+      // half's MFMAs so that the matrix core restarts right after the
+      // barrier (measured: latent + router 239.9 against 245.8 us, 4
+      // interleaved pairs); the latent GEMM issues them together, because
+      // spreading them there spills 42 registers.
+      if (!Router && kt + 3 < kGKT) issue(kt + 3);
+      step(o, false, true, stage_lds(kt + 1), 0, Router && kt + 3 < kGKT ? kt + 3 : -1);
     }
     // fold the restarted chains into the long sums
 #pragma unroll
