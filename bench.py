@@ -328,8 +328,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": f"decode_route_kernel<{1 if args.rows <= 16 else 2}, DecodeShape<3584, 896, 8, 8>, "
-                          f"true> (packed weights)",
+                "kernel": f"decode_route_kernel<{1 if args.rows <= 16 else 2}, DecodeShape<3584, 896, "
+                          f"{'8, 8' if args.rows <= 4 else '4, 8'}>, true> (packed weights)",
                 "kernel_us_per_launch": round(kernel_ms * 1000.0, 3),
                 "algorithmic_bytes_per_launch": decode_bytes(args.rows)}
 

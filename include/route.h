@@ -164,11 +164,11 @@ int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t sh
  *     loads (the [K][N] layouts give it strided 128-byte row segments);
  *     77,070,336 bytes: the latent weight's 51,380,224 bytes of BF16 values,
  *     then the router weight's 25,690,112 bytes of FP32 values, each tile in
- *     K order. The kernel splits K 8 ways for both weights, so that every
- *     wave streams the same bytes; this K split differs from the [K][N]
- *     kernel's, so a latent value may differ from route_fused's in the last
- *     bit (each is one full-K dot rounded once). Logits are FP64 sums rounded
- *     once in both;
+ *     K order. The kernel splits K its own ways (8 for both weights up to 4
+ *     rows, 4 for the latent and 8 for the router above); this K split
+ *     differs from the [K][N] kernel's, so a latent value may differ from
+ *     route_fused's in the last bit (each is one full-K dot rounded once).
+ *     Logits are FP64 sums rounded once in both;
  *   prefill: the weights K-contiguous, W as [3584][7168] BF16 (the [out][in]
  *     layout of a linear layer) and the router weight as its three exact
  *     BF16 parts [2688][7168] (split once here instead of on every call), so

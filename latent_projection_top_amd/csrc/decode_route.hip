@@ -13,8 +13,8 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split (whole route with [K][N] weights; packed weights split both
-// weights' K 8 ways instead, 224 router then 448 latent workgroups, see
+// Work split (whole route with [K][N] weights; packed weights split K 8 ways
+// for both weights up to 4 rows and 4 (latent) / 8 (router) ways above, see
 // PackedShape; a tensor-parallel rank's share uses the same units over its
 // columns with more K splits): 672 workgroups of 4 waves, all resident at
 // once.
@@ -100,36 +100,43 @@ struct DecodeShape {
   static_assert(N % 4 == 0 && E % 2 == 0, "a lane's loads stay inside a row");
 };
 using FullShape = DecodeShape<kLatent, kExperts, 4, 16>;
-// With packed weights every unit's block is contiguous, and 8 K splits of
-// both weights, which give every wave the same 28 KB to stream (224 router +
-// 448 latent workgroups, all resident), with the latent hold and the router
-// prefetch depth below, were measured faster than 4 x 16 at every width (1 /
-// 8 / 12 / 16 / 20 rows: 17.5 / 18.7 / 19.5 / 20.3 / 21.8 us against 18.7 /
-// 20.0 / 20.9 / 20.9 / 22.9); with [K][N] weights 4 x 16 is faster at every
-// width.
-using PackedShape = DecodeShape<kLatent, kExperts, 8, 8>;
+// With packed weights every unit's block is contiguous and any K split reads
+// contiguous ranges, so the split is chosen by rows (graph over 8 weight
+// copies, us per route, each with the latent hold and router prefetch below):
+//   rows          1     2     4     8    12    16    17    20
+//   8 x 8       17.5  17.5  18.0  18.8  19.5  20.2  21.7  21.8
+//   4 x 8       18.0  18.0  18.0  18.5  19.2  19.7  21.0  21.2
+//   4 x 16      18.7    -     -   20.0  20.9  20.9    -   22.9
+// 8 x 8 gives every wave the same 28 KB to stream; 4 x 8 gives the latent
+// waves twice the router waves' bytes. With [K][N] weights 4 x 16 is faster
+// at every width.
+using PackedShape = DecodeShape<kLatent, kExperts, 8, 8>;      // 1..4 rows
+using PackedWideShape = DecodeShape<kLatent, kExperts, 4, 8>;  // 5..20 rows
+constexpr int kPackedNarrowMaxRows = 4;
 
-// Latent units of the packed 8 x 8 launch hold their stream back for 2.6 us
-// (260 ticks of the 100 MHz realtime counter) after they start, so that the
-// router's stream, which feeds the longer chain of dependent steps (tile
-// combine, router completion, top-16), has the memory to itself first; the
-// latent units, whose chain after the stream is shorter, still end in time.
-// Measured (graph over 8 weight copies): 1 / 2 / 4 / 8 / 9 rows 17.2 / 17.5 /
-// 18.1 / 19.0 / 19.45 us against 18.2 / 18.6 / 18.9 / 19.15 / 19.6 without
-// the hold; 2.0 and 3.2 us holds were slower than 2.6. With 4 x 16 splits
-// (16 router splits: the router stream already ends first) a hold did not
-// help. A bounded wait on a clock, not on another workgroup.
-template <class Sh>
-constexpr uint64_t latent_hold_ticks() { return Sh::SplitsL == 8 && Sh::SplitsR == 8 ? 260 : 0; }
+// Latent units of a packed launch (8 router splits) hold their stream back
+// after they start, 2.6 us up to 16 rows and 3.6 us at 17..20 rows (ticks of
+// the 100 MHz realtime counter), so that the router's stream, which feeds the
+// longer chain of dependent steps (tile combine, router completion, top-16),
+// has the memory to itself first; the latent units, whose chain after the
+// stream is shorter, still end in time. Measured (8 x 8, 1 / 4 / 8 rows):
+// 17.2 / 18.1 / 19.0 us against 18.2 / 18.9 / 19.15 without it; holds of 2.0
+// and 3.2 us were slower than 2.6. 4 x 8 at 17 / 20 rows: 26.2 / 25.5 us
+// without a hold, 25.3 / 25.0 with 1.8 us, 22.7 / 22.6 with 2.6, 21.0 / 21.2
+// with 3.6 and 21.4 / 21.9 with 4.5. With 16 router splits (the router
+// stream already ends first) a hold did not help. A bounded wait on a clock,
+// not on another workgroup.
+template <int NT, class Sh>
+constexpr uint64_t latent_hold_ticks() { return Sh::SplitsR == 8 ? (NT == 1 ? 260 : 360) : 0; }
 
-// Router steps of loads kept in flight per wave. The 8 x 8 launch's router
-// waves have 14 steps and, while the latent units hold, the memory to
-// themselves: all 14 in flight up to 16 rows (8 / 12 rows 0.3 us faster than
-// 7), 10 at 17..20 rows (14 spill registers there). Otherwise up to 7 (all of
-// a 4 x 16 router wave's).
+// Router steps of loads kept in flight per wave. With 8 router splits a
+// router wave has 14 steps and, while the latent units hold, the memory to
+// itself: all 14 in flight up to 16 rows (8 / 12 rows 0.3 us faster than 7),
+// 10 at 17..20 rows (14 spill registers there). Otherwise up to 7 (all of a
+// 16-split router wave's).
 template <int NT, class Sh>
 constexpr int router_depth() {
-  const int d = (Sh::SplitsL == 8 && Sh::SplitsR == 8) ? (NT == 1 ? 14 : 10) : 7;
+  const int d = Sh::SplitsR == 8 ? (NT == 1 ? 14 : 10) : 7;
   return Sh::StepsR < d ? Sh::StepsR : d;
 }
 // Share splits measured on MI355X (graph-replayed launches over 616 MB of
@@ -139,7 +146,7 @@ using Tp8Shape = DecodeShape<448, 112, 7, 28>;
 using Tp16Shape = DecodeShape<224, 56, 14, 28>;
 constexpr int kDecodeCounters = FullShape::Counters;   // the largest counter set
 static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters &&
-                  PackedShape::Counters == kDecodeCounters,
+                  PackedShape::Counters == kDecodeCounters && PackedWideShape::Counters == kDecodeCounters,
               "every shape's counters fit the workspace's counter area");
 static_assert(FullShape::LatTiles == 56 && FullShape::RtTiles == 28 && FullShape::Grid == 672, "full shape");
 
@@ -448,9 +455,9 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (Packed && latent_hold_ticks<Sh>() > 0) {
+  if constexpr (Packed && latent_hold_ticks<NT, Sh>() > 0) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__builtin_amdgcn_s_memrealtime() - t0 < latent_hold_ticks<Sh>()) __builtin_amdgcn_s_sleep(2);
+    while (__builtin_amdgcn_s_memrealtime() - t0 < latent_hold_ticks<NT, Sh>()) __builtin_amdgcn_s_sleep(2);
   }
   constexpr int kDepth = depth<NT>() < Sh::StepsL ? depth<NT>() : Sh::StepsL;
   u32x2 wv[kDepth][8];
@@ -655,9 +662,9 @@ void decode_route_kernel(DecodeArgs a) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Sh2: a second shape sharing the workspace (the whole route's 8 x 8 packed
-// launch shares the [K][N] launch's counters and partial areas); each partial
-// area fits the larger of the two.
+// Sh2: a second shape sharing the workspace (the whole route's packed
+// launches share the [K][N] launch's counters and partial areas); each
+// partial area fits the larger of the two.
 template <class Sh, class Sh2 = Sh>
 static size_t ws_bytes(int rows_cap, size_t* off_lat, size_t* off_rt, size_t* off_logits, size_t* off_cand) {
   constexpr int kSL = Sh::SplitsL > Sh2::SplitsL ? Sh::SplitsL : Sh2::SplitsL;
@@ -687,6 +694,9 @@ size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off
     return ws_bytes<Tp8Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
   if (latent == Tp16Shape::N && experts == Tp16Shape::E)
     return ws_bytes<Tp16Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
+  static_assert(PackedWideShape::SplitsL <= PackedShape::SplitsL &&
+                    PackedWideShape::SplitsR <= FullShape::SplitsR,
+                "the 4 x 8 packed launch fits the partial areas of the other two");
   return ws_bytes<FullShape, PackedShape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
 }
 
@@ -720,8 +730,10 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (full && packed)
+  if (full && packed && rows <= kPackedNarrowMaxRows)
     launch_shape<PackedShape, true>(a, rows, stream);
+  else if (full && packed)
+    launch_shape<PackedWideShape, true>(a, rows, stream);
   else if (full)
     launch_shape<FullShape>(a, rows, stream);
   else if (n_latent == Tp8Shape::N)
@@ -738,11 +750,11 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
 // the whole-route kernel's lanes consume them, so that every unit streams one
 // contiguous block and every load instruction covers 1 KB with one 16-byte
 // piece per lane. Each tile's data is in K order, so that a unit of any K
-// split reads one contiguous range. The packed kernel splits K 8 ways for both
-// weights (PackedShape) where the [K][N] kernel splits the latent 4 and the
-// router 16 ways, so the latent's last bit may differ from route_fused's
-// (both are one full-K dot rounded once, within the same bounds); its logits
-// are FP64 sums rounded once, as there.
+// split reads one contiguous range. The packed kernel splits K its own ways
+// (PackedShape, PackedWideShape) where the [K][N] kernel splits the latent 4
+// and the router 16 ways, so the latent's last bit may differ from
+// route_fused's (both are one full-K dot rounded once, within the same
+// bounds); its logits are FP64 sums rounded once, as there.
 //
 // Latent: tile t (64 columns), K step s (32 rows), MFMA c, lane (g, m) =
 // (l / 16, l mod 16): 8 BF16 values W[32 s + 8 g + i][64 t + 4 m + c],

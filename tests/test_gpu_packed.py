@@ -3,7 +3,8 @@ route_fused_packed) on the GPU through the C ABI.
 
 A decode buffer holds the [K][N] weights' values in the packed decode
 kernel's consumption order, tile by tile in K order (the kernel splits K 8
-ways for both weights); a prefill buffer holds W transposed and the router
+ways for both weights up to 4 rows, 4 / 8 ways above); a prefill buffer
+holds W transposed and the router
 weight's three exact BF16 parts, transposed. Decode: the packed kernel's K
 split differs from route_fused's (latent 4, router 16 ways), so its outputs
 are checked against the oracle like route_fused's (latent
@@ -94,7 +95,7 @@ def run_packed_banks(width: int, banks: int, fused: bool, seed: int = 7000):
     return xs, out.host(), ws
 
 
-@pytest.mark.parametrize("width", [1, 8, 9, 12, 16, 20])
+@pytest.mark.parametrize("width", [1, 4, 5, 8, 9, 12, 16, 17, 20])
 def test_packed_decode_banks(width):
     log(f"packed decode parity width={width} banks={BANKS}")
     xs, got, ws = run_packed_banks(width, BANKS, fused=(width % 2 == 0))
@@ -102,7 +103,7 @@ def test_packed_decode_banks(width):
     assert decode_counters_idle(ws)
 
 
-@pytest.mark.parametrize("width", [1, 2, 8, 12, 13, 16, 17, 20])
+@pytest.mark.parametrize("width", [1, 2, 4, 5, 8, 12, 13, 16, 17, 20])
 def test_packed_fused_equals_two_calls_bitwise(width):
     _, a, _ = run_packed_banks(width, 3, fused=True, seed=7500)
     _, b, _ = run_packed_banks(width, 3, fused=False, seed=7500)
@@ -111,7 +112,7 @@ def test_packed_fused_equals_two_calls_bitwise(width):
     assert np.array_equal(a["weights"].view(np.uint32), b["weights"].view(np.uint32))
 
 
-@pytest.mark.parametrize("width", [1, 8, 12, 13, 17, 20])
+@pytest.mark.parametrize("width", [1, 4, 5, 8, 13, 17, 20])
 def test_packed_against_kn_on_one_workspace(width):
     """route_fused and route_fused_packed alternate on one workspace (they
     share its counters): every call's outputs stay right, the counters idle;

@@ -208,10 +208,11 @@ def test_share_graph_replay(ranks):
 
 @pytest.mark.timeout(600)
 def test_packed_graph_replay_mixed_widths_one_workspace():
-    """route_fused_packed at 1, 8, 13 and 20 rows (both packed launch shapes)
-    on one workspace, captured in one HIP graph with the outputs poisoned
-    inside it; every replay takes new banks and must equal the eager calls."""
-    widths = (1, 8, 13, 20)
+    """route_fused_packed at 1, 4, 5, 8, 13 and 20 rows (every packed launch
+    shape and hold) on one workspace, captured in one HIP graph with the
+    outputs poisoned inside it; every replay takes new banks and must equal
+    the eager calls."""
+    widths = (1, 4, 5, 8, 13, 20)
     replays = 500
     log(f"packed graph replay stress widths={widths} replays={replays}")
     w, wr = weights_dev(0)
