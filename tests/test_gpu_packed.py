@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 
 route = pytest.importorskip("latent_projection_top_amd.route")
 
-BANKS = 100
+BANKS = 200
 
 
 def packed_weights(copy: int = 0):
