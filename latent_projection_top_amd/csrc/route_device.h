@@ -78,12 +78,15 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 // --------------------------------------------------------------- top-16 --
 
 // Unsigned key whose order is the logit order: -0.0 maps onto +0.0, NaN onto 0
-// (below -inf, whose key is 0x007FFFFF).
+// (below -inf, whose key is 0x007FFFFF). Adding +0.0 turns -0.0 into +0.0 and
+// leaves every other number as it is (FP32 subnormals are kept); then a
+// positive value gets its top bit set and a negative one has every bit
+// inverted. No compare but the NaN test, so the 14 keys of a lane do not queue
+// on the condition register.
 __device__ __forceinline__ uint32_t logit_key(float v) {
-  uint32_t b = __float_as_uint(v);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
-  if ((b & 0x7FFFFFFFu) == 0u) return 0x80000000u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  const uint32_t flip = (uint32_t)((int32_t)b >> 31) | 0x80000000u;
+  return v != v ? 0u : (b ^ flip);
 }
 
 // Inverse of logit_key up to the sign of zero and the NaN payload, neither of
@@ -195,25 +198,37 @@ __device__ __forceinline__ uint32_t ballot_count(bool p) { return mask_count(bal
 
 // The largest t with at least `need` lanes holding v >= t among the lanes
 // where `in` is true, i.e. the need-th largest v of those lanes, built bit by
-// bit from the top (ballots and scalar counts only, no memory; measured
-// faster than two bits per step with three ballots).
+// bit from the top (ballots and scalar counts only; measured faster than two
+// bits per step with three ballots). As soon as exactly `need` lanes are at
+// or above the prefix, the answer is the smallest v among them, one wave
+// minimum away: on rows of random logits that happens after about 15 of the
+// 32 bits.
 __device__ __forceinline__ uint32_t nth_largest_u32(uint32_t v, bool in, uint32_t need) {
   uint32_t t = 0;
+  bool exact = false;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = t | (1u << b);
-    if (ballot_count(in && v >= c) >= need) t = c;
+    const uint32_t n = ballot_count(in && v >= c);
+    if (n >= need) {
+      t = c;
+      if (n == need) {
+        exact = true;
+        break;
+      }
+    }
   }
-  return t;
+  return exact ? ~wave_max_u32(in && v >= t ? ~v : 0u) : t;
 }
 
 // One wave selects the 16 largest of a set of distinct 64-bit keys, P per
 // lane (a zero key is padding: it is below every real key). At least 16
 // lanes must hold a real key. Returns, in lane s < 16, the s-th largest key.
-//   1. Threshold: t0 = the 16th largest of the 64 lane maxima, found with a
-//      bitwise search on the logit half (32 ballots) and, only when several
-//      lane maxima share that logit, on the index half among them. At least
-//      16 keys are >= t0, so the top 16 are among them.
+//   1. Threshold: t0 = the 16th largest of the 64 lanes' largest logit
+//      halves, found with a bitwise search (32 ballots), over a zero index
+//      half; only when several lanes share that largest logit half does a
+//      second search narrow the index half among them. At least 16 keys are
+//      >= t0, and the top 16 are among them.
 //   2. The keys >= t0 (typically about 20) are compacted into LDS in ballot
 //      order; each ranks itself against all of them, and rank r < 16 is the
 //      r-th selected key.
@@ -227,27 +242,30 @@ __device__ __forceinline__ uint32_t nth_largest_u32(uint32_t v, bool in, uint32_
 template <int P>
 __device__ __forceinline__ uint64_t select16(const uint64_t (&c)[P], uint64_t* scratch) {
   const int lane = threadIdx.x & (kWave - 1);
-  // lane maximum, pairwise
-  uint64_t m[P];
+  // lane maximum of the logit halves
+  uint32_t hm = (uint32_t)(c[0] >> 32);
 #pragma unroll
-  for (int i = 0; i < P; ++i) m[i] = c[i];
-#pragma unroll
-  for (int w = 1; w < P; w *= 2)
-#pragma unroll
-    for (int i = 0; i + w < P; i += 2 * w) m[i] = m[i + w] > m[i] ? m[i + w] : m[i];
-  const uint64_t mx = m[0];
+  for (int i = 1; i < P; ++i) hm = max(hm, (uint32_t)(c[i] >> 32));
 
-  // 1. the real lane maxima are distinct and at least 16 of them are above
-  //    every padding lane, so the 16th largest is one lane's maximum
-  const uint32_t hi = (uint32_t)(mx >> 32);
-  const uint32_t th = nth_largest_u32(hi, true, kTopK);
-  const uint64_t eq = ballot(hi == th);
-  uint64_t t0;
-  if (mask_count(eq) == 1u) {
-    t0 = readlane_u64(mx, __builtin_ctzll(eq));
-  } else {
-    const uint32_t need = kTopK - ballot_count(hi > th);
-    t0 = ((uint64_t)th << 32) | nth_largest_u32((uint32_t)mx, hi == th, need);
+  // 1. th is the 16th largest lane maximum of the logit halves: 16 lanes hold
+  //    a key whose logit half is >= th, and a key below th has at least 16
+  //    keys above it, so t0 = th:0 bounds the top 16 from below. When several
+  //    lane maxima share the logit half th, the index halves of those lanes'
+  //    64-bit maxima narrow it (otherwise every key of logit half th would
+  //    become a candidate, e.g. all 896 of a row of zeros).
+  const uint32_t th = nth_largest_u32(hm, true, kTopK);
+  const uint64_t eq = ballot(hm == th);
+  uint64_t t0 = (uint64_t)th << 32;
+  if (mask_count(eq) != 1u) {
+    uint64_t m[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) m[i] = c[i];
+#pragma unroll
+    for (int w = 1; w < P; w *= 2)
+#pragma unroll
+      for (int i = 0; i + w < P; i += 2 * w) m[i] = m[i + w] > m[i] ? m[i + w] : m[i];
+    const uint32_t need = kTopK - ballot_count(hm > th);
+    t0 |= nth_largest_u32((uint32_t)m[0], hm == th, need);
   }
 
   // 2. compaction: every ballot first, then the scalar prefix counts, then

@@ -71,6 +71,30 @@ def test_topk16_dense_ties_and_specials():
     assert compare.weights_check(w[fin], rw[fin])["fail"] == 0
 
 
+def test_topk16_subnormals_and_signed_zeros():
+    """Rows made of FP32 subnormals of both signs, signed zeros and a few
+    normal numbers: subnormals order as numbers (not as zero), -0.0 ties with
+    +0.0 and the lower index wins."""
+    log("topk16 subnormals and signed zeros")
+    plan = route.Plan(route.MODE_PREFILL, 256)
+    r = np.random.default_rng(13)
+    tiny = np.float32(np.finfo(np.float32).smallest_subnormal)
+    sub = (r.integers(1, 1 << 23, size=(256, 896)).astype(np.float32) * tiny).astype(np.float32)
+    sign = np.where(r.random((256, 896)) < 0.5, -1.0, 1.0).astype(np.float32)
+    L = (sub * sign).astype(np.float32)
+    z = r.random((256, 896))
+    L[z < 0.1] = np.float32(-0.0)
+    L[(z >= 0.1) & (z < 0.2)] = np.float32(0.0)
+    L[z > 0.999] = np.float32(1e-30)
+    # rows 0..63: only 20 positive subnormals, the rest zeros of both signs,
+    # so the zero ties decide the last places
+    L[:64] = np.where(r.random((64, 896)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    for i in range(64):
+        L[i, r.permutation(896)[:12]] = tiny * r.integers(1, 100, size=12).astype(np.float32)
+    assert (np.abs(L[L != 0]) < np.finfo(np.float32).tiny).mean() > 0.99
+    check(L, *run_topk(plan, L))
+
+
 def clustered_rows(n, seed):
     """Rows whose largest logits sit in 16 of the 64 lanes (expert index mod
     64): one lane all 10.0, fifteen lanes uniform in [10.5, 11]. The 16th
