@@ -95,6 +95,23 @@ def test_topk16_subnormals_and_signed_zeros():
     check(L, *run_topk(plan, L))
 
 
+def test_topk16_quantised_logits():
+    """Logits on coarse grids (steps 1/2, 1/8, 1/64, 1/1024 over a normal
+    spread): many equal values within and across lanes, so the threshold
+    often falls on a value several lane maxima share (the index-half search)
+    and the exact-count stop of the logit-half search fires rarely. ids must
+    equal the oracle's (lowest index first among equal logits)."""
+    log("topk16 quantised logits")
+    plan = route.Plan(route.MODE_PREFILL, 3072)
+    r = np.random.default_rng(14)
+    parts = []
+    for step in (0.5, 0.125, 1 / 64, 1 / 1024):
+        L = r.standard_normal((768, 896)) * 1.5
+        parts.append((np.round(L / step) * step).astype(np.float32))
+    L = np.concatenate(parts)
+    check(L, *run_topk(plan, L))
+
+
 def clustered_rows(n, seed):
     """Rows whose largest logits sit in 16 of the 64 lanes (expert index mod
     64): one lane all 10.0, fifteen lanes uniform in [10.5, 11]. The 16th
