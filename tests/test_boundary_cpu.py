@@ -173,3 +173,11 @@ def test_run_calls_reject_null_plan():
     assert route.LIB.route_latent_router_packed(None, None, None, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_fused_packed(None, None, None, None, None, None, None, None, 1, None) == route.E_ARG
     route.LIB.route_destroy(None)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """No fallback: with the shared library absent, loading the binding raises
+    instead of computing anything another way."""
+    monkeypatch.setattr(route, "LIB_PATH", str(tmp_path / "libroute.so"))
+    with pytest.raises(ImportError, match="not built"):
+        route._load()
