@@ -38,6 +38,7 @@ Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -150,6 +151,42 @@ def time_graph(g, replays: int, torch):
     return start.elapsed_time(end) / replays
 
 
+def read_sclk_mhz(path: str):
+    """Current shader clock in MHz from the driver's DPM table (the line
+    marked '*'), or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def sample_sclk(enqueue, torch, samples: int = 40):
+    """Shader clock while the GPU runs a workload: `enqueue` queues a few ms
+    of work without waiting for it; the clock is read from sysfs after each
+    batch, while the GPU is still busy with it. Runs outside every timed
+    window (reading the DPM table is a file read, no child process)."""
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+    torch.cuda.synchronize()
+    vals = []
+    for _ in range(samples):
+        enqueue()
+        v = read_sclk_mhz(paths[0])
+        if v is not None:
+            vals.append(v)
+    torch.cuda.synchronize()
+    if not vals:
+        return None
+    vals.sort()
+    return {"median_mhz": vals[len(vals) // 2], "min_mhz": vals[0], "max_mhz": vals[-1],
+            "samples": len(vals), "source": paths[0]}
+
+
 def capture_graph(fn, torch):
     """fn() run once on a side stream, then captured into a HIP graph."""
     s = torch.cuda.Stream()
@@ -254,7 +291,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=800, help="timed steps (multiple of 8)")
-    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--warmup", type=int, default=80, help="untimed steps per decode graph")
+    ap.add_argument("--clock-warmup-s", type=float, default=0.3,
+                    help="the headline graph's warm-up runs at least this long: the shader clock "
+                         "leaves its idle level only after about 0.2 s of load")
     ap.add_argument("--rows", type=int, default=8)
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--widths", default="1,8,9,12,16,20")
@@ -301,6 +341,7 @@ def main():
     widths = [args.rows] + ([int(w) for w in args.widths.split(",") if int(w) != args.rows]
                             if not args.no_extras else [])
     head = None
+    clocks = {}
     packs = pack_copies(copies, route, torch)
     for rows in widths:
         variants = [("packed", PackedDecodeSetup(rows, copies, banks, route, torch, packs))]
@@ -312,6 +353,15 @@ def main():
             for _ in range(reps_w):
                 g.replay()
             torch.cuda.synchronize()
+            if head is None:
+                # the first graph: keep replaying (untimed) until the clock is up
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < args.clock_warmup_s:
+                    for _ in range(50):
+                        g.replay()
+                    reps_w += 50
+                    torch.cuda.synchronize()
+                warm_head = reps_w * copies_n
             reps = steps // copies_n
             ms_rep = time_graph(g, reps, torch)
             us = ms_rep * 1000.0 / copies_n
@@ -320,6 +370,7 @@ def main():
                 f"({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
             if rows == args.rows and name == "packed":
                 head = (us, ms_rep / copies_n, ms_rep / copies_n)
+                clocks["decode"] = sample_sclk(lambda: [g.replay() for _ in range(25)], torch)
             del g, d
 
     us8, ms_step, kernel_ms = head
@@ -371,6 +422,8 @@ def main():
         t_all = t_call(lambda: route.fused_packed(plan, x, packed, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr = t_call(lambda: route.latent_router_packed(plan, x, packed, lat, lg, ws), args.prefill_reps)
         t_tk = t_call(lambda: route.topk16(plan, lg, ids, wt), args.prefill_reps)
+        clocks["prefill_gemms"] = sample_sclk(
+            lambda: [route.latent_router_packed(plan, x, packed, lat, lg, ws) for _ in range(10)], torch)
         t_all_kn = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr_kn = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
         del packed
@@ -408,7 +461,7 @@ def main():
         "unit": "us",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warm,
+        "warmup": warm_head,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -434,6 +487,9 @@ def main():
         "decode_kn_us_by_rows": {str(k): round(v, 3) for k, v in sorted(kn_results.items())},
         "prefill": prefill,
         "rank_share_decode": shares,
+        "sclk": dict(clocks, note="shader clock (MHz) sampled from the driver's DPM table while "
+                                  "the same workload ran, outside the timed windows; the peaks "
+                                  "above assume 2400 MHz"),
     }
     print(json.dumps(out), flush=True)
 
