@@ -1,0 +1,24 @@
+"""Host-side pieces of bench.py that need no GPU: the shader-clock reader and
+the algorithmic byte count of a decode route."""
+import bench
+
+
+def test_sclk_reader_takes_the_marked_line(tmp_path):
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text("S: 97Mhz\n0: 500Mhz\n1: 2400Mhz *\n")
+    assert bench.read_sclk_mhz(str(p)) == 2400
+    p.write_text("S: 97Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(p)) == 97
+    p.write_text("0: 500Mhz\n1: 1325Mhz *\n2: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(p)) == 1325
+    p.write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(p)) is None
+    assert bench.read_sclk_mhz(str(tmp_path / "absent")) is None
+
+
+def test_decode_bytes_formula():
+    # both weights once (51,380,224 + 25,690,112 bytes) plus, per row, the
+    # hidden row, latent, logits, ids and weights
+    assert bench.decode_bytes(1) == 77_070_336 + 25_216
+    assert bench.decode_bytes(8) == 77_272_064
+    assert bench.decode_bytes(20) - bench.decode_bytes(19) == 14_336 + 7_168 + 3_584 + 64 + 64
