@@ -143,18 +143,29 @@ class Plan:
             pass
 
 
-def _ptr(t: torch.Tensor | None, dtype, shape=None, name: str = "") -> int | None:
+def _ptr(t: torch.Tensor | None, dtype, shape=None, name: str = "", device: int | None = None) -> int | None:
     if t is None:
         return None
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name}: must be a contiguous device tensor")
+    if device is not None and t.device.index != device:
+        raise ValueError(f"{name}: on cuda:{t.device.index}, the plan is for cuda:{device}")
     if shape is not None and tuple(t.shape[1:]) != tuple(shape[1:]):
         raise ValueError(f"{name}: expected trailing shape {shape[1:]}, got {tuple(t.shape)}")
     if shape is not None and t.shape[0] < shape[0]:
         raise ValueError(f"{name}: needs at least {shape[0]} rows, has {t.shape[0]}")
     return t.data_ptr()
+
+
+def _ws_ptr(plan: Plan, workspace) -> int:
+    """The workspace must hold the plan's route_workspace_bytes: the kernels
+    write partials, counters and candidates across all of it."""
+    if workspace.numel() * workspace.element_size() < plan.workspace_bytes:
+        raise ValueError(f"workspace: needs {plan.workspace_bytes} bytes, has "
+                         f"{workspace.numel() * workspace.element_size()}")
+    return _ptr(workspace, torch.uint8, None, "workspace", plan.device)
 
 
 def _stream(stream) -> int | None:
@@ -167,12 +178,12 @@ def latent_router(plan: Plan, x, w_latent, w_router, latent, logits, workspace,
     rows = x.shape[0] if rows is None else rows
     st = LIB.route_latent_router(
         ctypes.c_void_p(plan.handle),
-        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
-        _ptr(w_latent, torch.bfloat16, (HIDDEN, plan.latent), "w_latent"),
-        _ptr(w_router, torch.float32, (HIDDEN, plan.experts), "w_router"),
-        _ptr(latent, torch.bfloat16, (rows, plan.latent), "latent"),
-        _ptr(logits, torch.float32, (rows, plan.experts), "logits"),
-        _ptr(workspace, torch.uint8, None, "workspace"),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x", plan.device),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, plan.latent), "w_latent", plan.device),
+        _ptr(w_router, torch.float32, (HIDDEN, plan.experts), "w_router", plan.device),
+        _ptr(latent, torch.bfloat16, (rows, plan.latent), "latent", plan.device),
+        _ptr(logits, torch.float32, (rows, plan.experts), "logits", plan.device),
+        _ws_ptr(plan, workspace),
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_latent_router")
@@ -182,9 +193,9 @@ def topk16(plan: Plan, logits, ids, weights, rows: int | None = None, stream=Non
     rows = logits.shape[0] if rows is None else rows
     st = LIB.route_topk16(
         ctypes.c_void_p(plan.handle),
-        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
-        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
-        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits", plan.device),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids", plan.device),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights", plan.device),
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_topk16")
@@ -197,11 +208,11 @@ def topk16_sharded(plan: Plan, logits, shards: int, ids, weights, workspace, row
     rows = logits.shape[0] if rows is None else rows
     st = LIB.route_topk16_sharded(
         ctypes.c_void_p(plan.handle),
-        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits", plan.device),
         int(shards),
-        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
-        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
-        _ptr(workspace, torch.uint8, None, "workspace"),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids", plan.device),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights", plan.device),
+        _ws_ptr(plan, workspace),
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_topk16_sharded")
@@ -212,14 +223,14 @@ def fused(plan: Plan, x, w_latent, w_router, latent, logits, ids, weights, works
     rows = x.shape[0] if rows is None else rows
     st = LIB.route_fused(
         ctypes.c_void_p(plan.handle),
-        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
-        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent"),
-        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router"),
-        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
-        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
-        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
-        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
-        _ptr(workspace, torch.uint8, None, "workspace"),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x", plan.device),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent", plan.device),
+        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router", plan.device),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent", plan.device),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits", plan.device),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids", plan.device),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights", plan.device),
+        _ws_ptr(plan, workspace),
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_fused")
@@ -236,9 +247,9 @@ def pack_weights(plan: Plan, w_latent, w_router, packed=None, stream=None) -> to
         raise ValueError(f"packed: needs {plan.packed_bytes} uint8 elements")
     st = LIB.route_pack_weights(
         ctypes.c_void_p(plan.handle),
-        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent"),
-        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router"),
-        _ptr(packed, torch.uint8, None, "packed"),
+        _ptr(w_latent, torch.bfloat16, (HIDDEN, LATENT), "w_latent", plan.device),
+        _ptr(w_router, torch.float32, (HIDDEN, EXPERTS), "w_router", plan.device),
+        _ptr(packed, torch.uint8, None, "packed", plan.device),
         _stream(stream))
     if st != OK:
         raise RouteError(st, "route_pack_weights")
@@ -248,7 +259,7 @@ def pack_weights(plan: Plan, w_latent, w_router, packed=None, stream=None) -> to
 def _packed_ptr(plan: Plan, packed) -> int:
     if packed.numel() < plan.packed_bytes:
         raise ValueError(f"packed: needs {plan.packed_bytes} bytes, has {packed.numel()}")
-    return _ptr(packed, torch.uint8, None, "packed")
+    return _ptr(packed, torch.uint8, None, "packed", plan.device)
 
 
 def latent_router_packed(plan: Plan, x, packed, latent, logits, workspace, rows: int | None = None,
@@ -256,11 +267,11 @@ def latent_router_packed(plan: Plan, x, packed, latent, logits, workspace, rows:
     rows = x.shape[0] if rows is None else rows
     st = LIB.route_latent_router_packed(
         ctypes.c_void_p(plan.handle),
-        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x", plan.device),
         _packed_ptr(plan, packed),
-        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
-        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
-        _ptr(workspace, torch.uint8, None, "workspace"),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent", plan.device),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits", plan.device),
+        _ws_ptr(plan, workspace),
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_latent_router_packed")
@@ -271,13 +282,13 @@ def fused_packed(plan: Plan, x, packed, latent, logits, ids, weights, workspace,
     rows = x.shape[0] if rows is None else rows
     st = LIB.route_fused_packed(
         ctypes.c_void_p(plan.handle),
-        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x"),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x", plan.device),
         _packed_ptr(plan, packed),
-        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent"),
-        _ptr(logits, torch.float32, (rows, EXPERTS), "logits"),
-        _ptr(ids, torch.int32, (rows, TOPK), "ids"),
-        _ptr(weights, torch.float32, (rows, TOPK), "weights"),
-        _ptr(workspace, torch.uint8, None, "workspace"),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent", plan.device),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits", plan.device),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids", plan.device),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights", plan.device),
+        _ws_ptr(plan, workspace),
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_fused_packed")

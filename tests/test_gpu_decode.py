@@ -186,3 +186,33 @@ def test_zero_rows_degenerate_case():
             assert np.array_equal(h["ids"][r], np.arange(16))
             assert (h["weights"][r] == np.float32(1.0 / 16.0)).all()
         check_outputs(xs, h, f"decode w={width} with zero rows")
+
+
+def test_binding_rejects_short_workspace_and_wrong_device():
+    """The binding checks what the C ABI cannot see: a workspace shorter than
+    route_workspace_bytes, and tensors on another device than the plan's.
+    Nothing is launched."""
+    w, wr = weights_dev(0)
+    plan = route.Plan(route.MODE_DECODE, 8)
+    xd = bf16_dev(gen.hidden(8, bank=3))
+    o = Outputs(8)
+    o.poison()
+    short = torch.zeros(plan.workspace_bytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        route.fused(plan, xd, w, wr, o.latent, o.logits, o.ids, o.weights, short)
+    with pytest.raises(ValueError, match="workspace"):
+        route.latent_router(plan, xd, w, wr, o.latent, o.logits, short)
+    pplan = route.Plan(route.MODE_PREFILL, 64)
+    pshort = torch.zeros(pplan.workspace_bytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        route.latent_router(pplan, xd, w, wr, o.latent, o.logits, pshort, rows=8)
+    torch.cuda.synchronize()
+    assert (bits_host(o.latent) == 0xFFFF).all()
+    assert int(short.count_nonzero()) == 0
+    # a plan for another device index: every tensor here is on the current one
+    other = route.Plan.__new__(route.Plan)
+    other.__dict__.update(plan.__dict__)
+    other.device = plan.device + 1
+    other.handle = 0  # never reaches the library
+    with pytest.raises(ValueError, match="plan is for"):
+        route.fused(other, xd, w, wr, o.latent, o.logits, o.ids, o.weights, plan.new_workspace())
