@@ -172,6 +172,14 @@ def sample_sclk(enqueue, torch, samples: int = 40):
     paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
     if not paths:
         return None
+    # the card of the current device, by PCI address, when the runtime gives it
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is not None:
+        tag = f"{getattr(props, 'pci_domain_id', 0):04x}:{bus:02x}:{getattr(props, 'pci_device_id', 0):02x}."
+        mine = [p for p in paths if tag in os.path.realpath(os.path.dirname(p))]
+        if mine:
+            paths = mine
     torch.cuda.synchronize()
     vals = []
     for _ in range(samples):
