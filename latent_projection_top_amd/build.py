@@ -43,8 +43,29 @@ def _compile(src: str) -> str:
     return obj
 
 
+EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "route_example.c")
+EXAMPLE_EXE = os.path.join(BUILD_DIR, "route_example")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_example(verbose: bool = False) -> str:
+    """The C example (tests/c_abi/route_example.c): plain C99 over the HIP
+    runtime API and libroute.so, found next to the binary's directory."""
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), EXAMPLE_SRC,
+           "-L", HERE, "-lroute", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", EXAMPLE_EXE]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the C example failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {EXAMPLE_EXE}", file=sys.stderr)
+    return EXAMPLE_EXE
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libroute.so next to this file."""
+    """Compile every source and link libroute.so next to this file, then the
+    C example that links against it."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
@@ -56,6 +77,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}", file=sys.stderr)
+    build_example(verbose)
     return LIB_PATH
 
 
