@@ -79,7 +79,9 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 
 // Unsigned key whose order is the logit order: -0.0 maps onto +0.0, NaN onto 0
 // (below -inf, whose key is 0x007FFFFF). Adding +0.0 turns -0.0 into +0.0 and
-// leaves every other number as it is (FP32 subnormals are kept); then a
+// leaves every other number as it is (FP32 subnormals are kept: the kernels
+// run in IEEE denormal mode, and without fast-math flags the compiler keeps
+// the add, since x + 0.0 is not x for x = -0.0); then a
 // positive value gets its top bit set and a negative one has every bit
 // inverted. No compare but the NaN test, so the 14 keys of a lane do not queue
 // on the condition register.
