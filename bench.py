@@ -10,7 +10,10 @@ the weights rotate over 8 distinct copies (8 x 77 MB, more than the 256 MB
 Infinity Cache) so every step streams its weights from HBM. Steps are replayed
 from a HIP graph holding 8 calls (one per weight copy, each on its own input
 bank); K steps = K/8 replays, timed with events on the launch stream between
-two device synchronisations.
+two device synchronisations. Before the timing, the headline graph replays
+untimed for at least 0.3 s: the shader clock leaves its idle level only
+after about 0.2 s of load. The shader clock read from the driver's DPM table
+while each workload runs (outside the timed windows) is reported as `sclk`.
 
 Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows),
 each also through route_fused on the [K][N] weights, the 3072-row prefill
