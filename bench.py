@@ -7,34 +7,42 @@ parameters: each weight copy is packed once by route_pack_weights (the decode
 kernel's read order, same bytes) outside the timed region, as a server does
 when it loads the weights. The headline workload is the 8-row decode round;
 the weights rotate over 8 distinct copies (8 x 77 MB, more than the 256 MB
-Infinity Cache) so every step streams its weights from HBM. Steps are replayed
-from a HIP graph holding 8 calls (one per weight copy, each on its own input
-bank); K steps = K/8 replays, timed with events on the launch stream between
-two device synchronisations. Before the timing, the headline graph replays
-untimed for at least 0.3 s: the shader clock leaves its idle level only
-after about 0.2 s of load. The shader clock read from the driver's DPM table
-while each workload runs (outside the timed windows) is reported as `sclk`.
+Infinity Cache) so every step streams its weights from HBM.
+
+Timing protocol (the pages time graph replays and report medians of
+repeated windows): the routes are replayed from HIP graphs, one holding a
+call per weight copy (each on its own input bank) and, when --steps is not a
+multiple of the copies, one holding the remaining calls, so a window runs
+exactly --steps routes. --warmup routes run untimed first; then the headline
+graph keeps replaying, untimed, for at least --clock-warmup-s seconds (the
+shader clock leaves its idle level only after about 0.2 s of load; reported
+on its own as `clock_warmup`). --windows windows of --steps routes are timed
+with events on the launch stream between two device synchronisations, and
+the median window gives the value. The shader clock read from the driver's
+DPM table while each workload runs (outside the timed windows) is reported as
+`sclk`.
 
 Also reported: every decode width of the pages (1, 8, 9, 12, 16, 20 rows),
 each also through route_fused on the [K][N] weights, the 3072-row prefill
 chunk (packed weights, and the [K][N] path beside it), the decode kernel at
 one tensor-parallel rank's share (448 x 112 at 8 ranks, 224 x 56 at 16 ranks;
 1, 8 and 20 rows), the decode kernel's HBM roofline fraction, the prefill
-MFMA fraction, and the CPU oracle timed on this host (a reported baseline
+MFMA fractions, and the CPU oracle timed on this host (a reported baseline
 only).
 
-Roofline: a decode route is one kernel launch, so the kernel's average launch
-duration is the event-timed graph replay divided by the launches in it (it
-includes the ~1 us between back-to-back launches; event pairs around single
-launches would add far more). The algorithmic bytes of one launch (both
-weights once + the rows' inputs and outputs) divided by that duration is
-`achieved`. `traffic` is the HBM bytes
-per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
-valid only while the kernel source is unchanged.
+Roofline: a decode route is one kernel launch. `achieved` divides the
+algorithmic bytes of one launch (both weights once + the rows' inputs and
+outputs) by the launch interval measured here (median window / steps: the
+kernel's duration plus the ~1 us between back-to-back launches);
+`kernel_trace` divides the same bytes by the kernel's average dispatch
+duration in the committed rocprofv3 trace of this benchmark (no gaps), and
+`traffic` is the HBM bytes per launch from the committed FETCH_SIZE /
+WRITE_SIZE summary; both are read only while the kernel source is the one
+they were taken on.
 
 --profile-pass runs only what the counter runs need: 64 headline decode
-launches (packed weights) and a plain 512 MiB device copy (the counters'
-calibration).
+launches (packed weights), a plain 512 MiB device copy (the counters'
+calibration) and 8 packed prefill chunks.
 
 Prints ONE JSON line on stdout.
 """
@@ -58,8 +66,10 @@ K, N, E = 7168, 3584, 896
 FIXED_BYTES = K * N * 2 + K * E * 4                       # 77,070,336
 ROW_BYTES = K * 2 + N * 2 + E * 4 + 16 * 4 + 16 * 4       # 25,216
 PREFILL_FLOPS_LATENT = 2.0 * 3072 * K * N                 # 157.84 GFLOP
-PREFILL_FLOPS_ROUTER_MFMA = 3 * 2.0 * 3072 * K * E        # bf16 x3 split, 118.4 GFLOP
+PREFILL_FLOPS_ROUTER = 2.0 * 3072 * K * E                 # the method's router work, 39.46 GFLOP
+PREFILL_FLOPS_ROUTER_MFMA = 3 * PREFILL_FLOPS_ROUTER      # bf16 x3 split, 118.4 GFLOP of MFMA work
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_route_r8_counters.md")
+PROFILE_TRACE = os.path.join(ROOT, "profiles", "decode_route_r8_kernel_trace.md")
 DECODE_SOURCES = ["latent_projection_top_amd/csrc/decode_route.hip",
                   "latent_projection_top_amd/csrc/route_device.h"]
 
@@ -80,22 +90,30 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
-        return None
+def profile_fields(path: str) -> dict:
+    """The `- name: `value`` fields of a committed profile summary, if it was
+    taken on the current kernel source; else {}."""
+    if not os.path.exists(path):
+        return {}
     fields = {}
-    for line in open(PROFILE_COUNTERS):
+    for line in open(path):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_digest") != source_digest():
-        return None
+    return fields if fields.get("kernel_source_digest") == source_digest() else {}
+
+
+def committed_float(path: str, name: str):
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(profile_fields(path)[name])
     except (KeyError, ValueError):
         return None
+
+
+def committed_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    return committed_float(PROFILE_COUNTERS, "hbm_bytes_per_launch")
 
 
 class DecodeSetup:
@@ -114,14 +132,31 @@ class DecodeSetup:
         self.wt = torch.empty((n, rows, 16), dtype=torch.float32, device=dev)
         self.copies = copies
 
-    def run_all(self):
+    def run_all(self, count: int | None = None):
         r = self.route
-        for i, (w, wr) in enumerate(self.copies):
+        for i, (w, wr) in enumerate(self.copies[:count]):
             r.fused(self.plan, self.xs[i], w, wr, self.lat[i], self.lg[i], self.ids[i], self.wt[i],
                     self.ws[i], rows=self.rows)
 
-    def capture(self):
-        return capture_graph(self.run_all, self.torch)
+    def capture(self, count: int | None = None):
+        return capture_graph(lambda: self.run_all(count), self.torch)
+
+    def runner(self, counts):
+        """A function that replays exactly n routes (n in `counts`): the graph
+        of one call per weight copy n // copies times, then a graph of the
+        first n % copies calls. Every graph is captured here, before any
+        timing."""
+        n_copies = len(self.copies)
+        full = self.capture()
+        part = {c % n_copies: self.capture(c % n_copies) for c in counts if c % n_copies}
+
+        def run(n: int):
+            for _ in range(n // n_copies):
+                full.replay()
+            if n % n_copies:
+                part[n % n_copies].replay()
+        run.full = full
+        return run
 
 
 class PackedDecodeSetup(DecodeSetup):
@@ -133,25 +168,30 @@ class PackedDecodeSetup(DecodeSetup):
         super().__init__(rows, copies, banks_dev, route, torch)
         self.packs = packs
 
-    def run_all(self):
+    def run_all(self, count: int | None = None):
         r = self.route
-        for i, pk in enumerate(self.packs):
+        for i, pk in enumerate(self.packs[:count]):
             r.fused_packed(self.plan, self.xs[i], pk, self.lat[i], self.lg[i], self.ids[i], self.wt[i],
                            self.ws[i], rows=self.rows)
 
 
-def time_graph(g, replays: int, torch):
-    """Average ms per replay of `replays` back-to-back replays (events on the
-    current stream, which is the stream the graph's kernels run on)."""
+def time_routes(run, n: int, torch):
+    """ms of one window of exactly n routes (events on the current stream,
+    which is the stream the graphs' kernels run on, between two device
+    synchronisations)."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(replays):
-        g.replay()
+    run(n)
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / replays
+    return start.elapsed_time(end)
+
+
+def time_graph(g, replays: int, torch):
+    """Average ms per replay of `replays` back-to-back replays of one graph."""
+    return time_routes(lambda n: [g.replay() for _ in range(n)], replays, torch) / replays
 
 
 def read_sclk_mhz(path: str):
@@ -257,9 +297,25 @@ def pack_copies(copies, route, torch):
     return packs
 
 
-def profile_pass(rows: int, copies, banks, route, torch):
-    """Short run for the rocprofv3 counter passes: headline decode launches and
-    one plain copy of known size."""
+def prefill_inputs(route, torch, bf16, gen, w0, wr0):
+    """The 3072-row prefill chunk (1 % outlier channels) with its plan,
+    workspace, outputs and packed weights."""
+    rows = 3072
+    plan = route.Plan(route.MODE_PREFILL, rows)
+    p = {"plan": plan, "ws": plan.new_workspace(), "rows": rows,
+         "x": bf16(gen.hidden(rows, bank=4100, outliers=True)),
+         "lat": torch.empty((rows, N), dtype=torch.bfloat16, device="cuda"),
+         "lg": torch.empty((rows, E), dtype=torch.float32, device="cuda"),
+         "ids": torch.empty((rows, 16), dtype=torch.int32, device="cuda"),
+         "wt": torch.empty((rows, 16), dtype=torch.float32, device="cuda")}
+    p["packed"] = route.pack_weights(plan, w0, wr0)
+    torch.cuda.synchronize()
+    return p
+
+
+def profile_pass(rows: int, copies, banks, route, torch, bf16, gen):
+    """Short run for the rocprofv3 counter passes: headline decode launches,
+    one plain copy of known size, and packed prefill chunks."""
     d = PackedDecodeSetup(rows, copies, banks, route, torch, pack_copies(copies, route, torch))
     for _ in range(8):
         d.run_all()
@@ -268,7 +324,13 @@ def profile_pass(rows: int, copies, banks, route, torch):
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"profile pass: {8 * len(copies)} decode launches of {rows} rows, one 512 MiB copy")
+    del src, dst
+    p = prefill_inputs(route, torch, bf16, gen, *copies[0])
+    for _ in range(8):
+        route.fused_packed(p["plan"], p["x"], p["packed"], p["lat"], p["lg"], p["ids"], p["wt"], p["ws"])
+    torch.cuda.synchronize()
+    log(f"profile pass: {8 * len(copies)} decode launches of {rows} rows, one 512 MiB copy, "
+        f"8 packed 3072-row prefill chunks")
 
 
 def cpu_baseline(rows: int, budget_s: float):
@@ -301,11 +363,14 @@ def cpu_baseline(rows: int, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=800, help="timed steps (multiple of 8)")
-    ap.add_argument("--warmup", type=int, default=80, help="untimed steps per decode graph")
+    ap.add_argument("--steps", type=int, default=1600,
+                    help="routes per timed window (1600 = 200 replays of the 8-copy graph)")
+    ap.add_argument("--warmup", type=int, default=80, help="untimed routes before the timing")
+    ap.add_argument("--windows", type=int, default=5, help="timed windows; the median is reported")
     ap.add_argument("--clock-warmup-s", type=float, default=0.3,
-                    help="the headline graph's warm-up runs at least this long: the shader clock "
-                         "leaves its idle level only after about 0.2 s of load")
+                    help="after the warm-up routes, the headline graph replays untimed for at least "
+                         "this long: the shader clock leaves its idle level only after about 0.2 s "
+                         "of load")
     ap.add_argument("--rows", type=int, default=8)
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--widths", default="1,8,9,12,16,20")
@@ -322,6 +387,9 @@ def main():
         print("bench.py measures one GPU only: the route computes every row locally and has "
               "no multi-GPU path to time (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.windows < 1:
+        print("--steps and --windows must be positive and --warmup non-negative", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -331,8 +399,7 @@ def main():
 
     torch.cuda.set_device(0)
     copies_n = args.copies
-    steps = max(copies_n, (args.steps // copies_n) * copies_n)
-    warm = max(copies_n, (args.warmup // copies_n) * copies_n)
+    steps, warm = args.steps, args.warmup
 
     log(f"generating {copies_n} weight copies ...")
 
@@ -344,7 +411,7 @@ def main():
         copies.append((bf16(gen.latent_weight(c)), torch.from_numpy(gen.router_weight(c)).cuda()))
     banks = [bf16(gen.hidden(20, bank=4000 + b)) for b in range(copies_n)]
     if args.profile_pass:
-        profile_pass(args.rows, copies, banks, route, torch)
+        profile_pass(args.rows, copies, banks, route, torch, bf16, gen)
         return
 
     results = {}
@@ -353,69 +420,77 @@ def main():
                             if not args.no_extras else [])
     head = None
     clocks = {}
+    clock_warm = None
     packs = pack_copies(copies, route, torch)
     for rows in widths:
         variants = [("packed", PackedDecodeSetup(rows, copies, banks, route, torch, packs))]
         if not args.no_extras:
             variants.append(("kn", DecodeSetup(rows, copies, banks, route, torch)))
         for name, d in variants:
-            g = d.capture()
-            reps_w = warm // copies_n
-            for _ in range(reps_w):
-                g.replay()
+            run = d.runner([steps, warm])
+            if warm:
+                run(warm)
             torch.cuda.synchronize()
-            if head is None:
+            if clock_warm is None:
                 # the first graph: keep replaying (untimed) until the clock is up
                 t0 = time.perf_counter()
+                reps = 0
                 while time.perf_counter() - t0 < args.clock_warmup_s:
                     for _ in range(50):
-                        g.replay()
-                    reps_w += 50
+                        run.full.replay()
+                    reps += 50
                     torch.cuda.synchronize()
-                warm_head = reps_w * copies_n
-            reps = steps // copies_n
-            ms_rep = time_graph(g, reps, torch)
-            us = ms_rep * 1000.0 / copies_n
+                clock_warm = {"seconds": round(time.perf_counter() - t0, 3), "routes": reps * copies_n,
+                              "note": "untimed replays of the headline graph after the warm-up routes"}
+            windows = sorted(time_routes(run, steps, torch) for _ in range(args.windows))
+            ms_win = windows[len(windows) // 2]
+            us = ms_win * 1000.0 / steps
             (results if name == "packed" else kn_results)[rows] = us
             log(f"decode rows={rows} ({name} weights): {us:.2f} us per route "
-                f"({decode_bytes(rows) / us / 1e3:.0f} GB/s)")
+                f"({decode_bytes(rows) / us / 1e3:.0f} GB/s; windows "
+                f"{', '.join(f'{w * 1000.0 / steps:.2f}' for w in windows)})")
             if rows == args.rows and name == "packed":
-                head = (us, ms_rep / copies_n, ms_rep / copies_n)
-                clocks["decode"] = sample_sclk(lambda: [g.replay() for _ in range(25)], torch)
-            del g, d
+                head = {"us": us, "ms_step": ms_win / steps,
+                        "windows_us": [round(w * 1000.0 / steps, 3) for w in windows]}
+                clocks["decode"] = sample_sclk(lambda: [run.full.replay() for _ in range(25)], torch)
+            del run, d
 
-    us8, ms_step, kernel_ms = head
-    achieved = decode_bytes(args.rows) / (kernel_ms * 1e-3) / 1e9
-    traffic = committed_traffic()
+    us8 = head["us"]
+    nbytes = decode_bytes(args.rows)
+    achieved = nbytes / (us8 * 1e-6) / 1e9
+    trace_us = committed_float(PROFILE_TRACE, "kernel_avg_us")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic,
+                "traffic": committed_traffic(),
+                "frac_basis": "algorithmic bytes per launch / launch interval (median window / steps, "
+                              "kernel duration plus the gap between back-to-back launches)",
                 "kernel": f"decode_route_kernel<{1 if args.rows <= 16 else 2}, DecodeShape<3584, 896, "
                           f"{'8, 8' if args.rows <= 4 else '4, 8'}>, true> (packed weights)",
-                "kernel_us_per_launch": round(kernel_ms * 1000.0, 3),
-                "algorithmic_bytes_per_launch": decode_bytes(args.rows)}
+                "launch_interval_us": round(us8, 3),
+                "algorithmic_bytes_per_launch": nbytes,
+                "kernel_trace": None if trace_us is None else {
+                    "avg_dispatch_us": trace_us,
+                    "achieved": round(nbytes / (trace_us * 1e-6) / 1e9, 1),
+                    "frac": round(nbytes / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "source": "profiles/decode_route_r8_kernel_trace.md (rocprofv3 dispatch durations of "
+                              "the timed launches, no inter-launch gaps)"}}
 
     prefill = None
     if not args.no_extras:
-        rows = 3072
-        plan = route.Plan(route.MODE_PREFILL, rows)
-        ws = plan.new_workspace()
-        x = bf16(gen.hidden(rows, bank=4100, outliers=True))
-        lat = torch.empty((rows, N), dtype=torch.bfloat16, device="cuda")
-        lg = torch.empty((rows, E), dtype=torch.float32, device="cuda")
-        ids = torch.empty((rows, 16), dtype=torch.int32, device="cuda")
-        wt = torch.empty((rows, 16), dtype=torch.float32, device="cuda")
+        p = prefill_inputs(route, torch, bf16, gen, *copies[0])
+        plan, ws, x, lat, lg, ids, wt = (p[k] for k in ("plan", "ws", "x", "lat", "lg", "ids", "wt"))
+        rows = p["rows"]
         w0, wr0 = copies[0]
 
         def t_call(fn, reps):
             # the first calls after the decode phase run slower (clocks rise
             # under the compute-bound GEMMs): warm up for about 12 ms, then
-            # take the median of three timed windows
+            # take the median of five timed windows
             for _ in range(40):
                 fn()
             torch.cuda.synchronize()
             times = []
-            for _ in range(3):
+            for _ in range(5):
                 s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s.record()
                 for _ in range(reps):
@@ -423,13 +498,12 @@ def main():
                 e.record()
                 torch.cuda.synchronize()
                 times.append(s.elapsed_time(e) / reps * 1000.0)
-            return sorted(times)[1]
+            return sorted(times)[2]
 
         # packed weights (K-contiguous W, router parts split once) first: the
         # reported figure; then the [K][N] path, which splits the router
         # weight on every call
-        packed = route.pack_weights(plan, w0, wr0)
-        torch.cuda.synchronize()
+        packed = p["packed"]
         t_all = t_call(lambda: route.fused_packed(plan, x, packed, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr = t_call(lambda: route.latent_router_packed(plan, x, packed, lat, lg, ws), args.prefill_reps)
         t_tk = t_call(lambda: route.topk16(plan, lg, ids, wt), args.prefill_reps)
@@ -437,14 +511,21 @@ def main():
             lambda: [route.latent_router_packed(plan, x, packed, lat, lg, ws) for _ in range(10)], torch)
         t_all_kn = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr_kn = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
-        del packed
-        gemm_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER_MFMA
+        del packed, p
+        method_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER
+        mfma_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER_MFMA
         prefill = {
             "rows": rows, "weights": "packed (route_pack_weights, once per weight set)",
             "us_per_chunk": round(t_all, 2), "rows_per_s": round(rows / (t_all * 1e-6)),
             "latent_router_us": round(t_lr, 2), "topk16_us": round(t_tk, 2),
-            "mfma_tflops": round(gemm_flops / (t_lr * 1e-6) / 1e12, 1),
-            "mfma_frac": round(gemm_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "method_tflops": round(method_flops / (t_lr * 1e-6) / 1e12, 1),
+            "method_frac": round(method_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_work_tflops": round(mfma_flops / (t_lr * 1e-6) / 1e12, 1),
+            "mfma_work_frac": round(mfma_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "flops_note": "method: 2*M*K*(3584+896) = 197.3 GFLOP; MFMA work: the router runs on three "
+                          "exact BF16 parts of its FP32 weight, 276.2 GFLOP; both over latent_router_us "
+                          "(the two GEMMs and the non-finite logit check); per-kernel times are in "
+                          "profiles/prefill_gemm_3072_kernel_trace.md",
             "router_variant": "FP32 weight split into 3 exact BF16 parts, BF16 MFMA, FP32 chains "
                               "restarted every 256 K and folded into FP64",
             "kn_weights": {"us_per_chunk": round(t_all_kn, 2),
@@ -453,7 +534,8 @@ def main():
                            "note": "[K][N] weights; includes the per-call router weight split"},
         }
         log(f"prefill 3072 (packed): {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
-            f"{t_lr:.1f} us = {prefill['mfma_tflops']} TFLOP/s, top-16 {t_tk:.1f} us; [K][N] weights "
+            f"{t_lr:.1f} us = {prefill['method_tflops']} TFLOP/s of the method's work "
+            f"({prefill['mfma_work_tflops']} of MFMA work), top-16 {t_tk:.1f} us; [K][N] weights "
             f"{t_all_kn:.1f} us")
 
     shares = None
@@ -472,12 +554,19 @@ def main():
         "unit": "us",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warm_head,
-        "ms_per_step": round(ms_step, 6),
+        "warmup": warm,
+        "ms_per_step": round(head["ms_step"], 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp32",
+        "precision": {
+            "latent": "BF16 x BF16 products, FP32 MFMA accumulation, K-split partials summed in FP64, "
+                      "rounded once to BF16",
+            "router": "FP32 weight x BF16 hidden value, accumulated in FP64 (decode; prefill: exact "
+                      "three-part BF16 split on the BF16 MFMA, FP32 chains of 256 K folded into FP64), "
+                      "rounded once to FP32",
+            "top16": "32-bit integer keys of the FP32 logits; weights in FP64, rounded to FP32"},
         "data": "synthetic",
         "config": {
             "workload": f"decode route, {args.rows} rows: x[{args.rows},7168] BF16 -> latent "
@@ -488,8 +577,11 @@ def main():
             "hidden": K, "latent": N, "experts": E, "topk": 16,
             "weight_copies": copies_n,
             "weights": "packed once per copy by route_pack_weights, outside the timed region",
-            "timing": "HIP graph of 8 route_fused_packed calls, events on the launch stream",
+            "timing": f"median of {args.windows} windows of exactly {steps} route_fused_packed calls "
+                      f"replayed from HIP graphs, events on the launch stream",
         },
+        "windows_us": head["windows_us"],
+        "clock_warmup": clock_warm,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode_us_by_rows": {str(k): round(v, 3) for k, v in sorted(results.items())},

@@ -26,7 +26,8 @@
  * plans accept 1..20 rows (the same page, "What / why": rounds of 1..20 rows
  * are prepared, anything else raises at preparation), prefill plans 1..3072
  * rows (the 3072-row chunk of pull request 16's timing table). There is no
- * fallback: every error is a negative status and nothing is launched.
+ * fallback: every error is a negative status, and an argument error launches
+ * nothing.
  *
  * Ownership and threading:
  *   - the caller owns every device buffer (inputs, weights, outputs,
@@ -86,7 +87,8 @@ extern "C" {
 #define ROUTE_DECODE_MAX_ROWS 20
 #define ROUTE_PREFILL_MAX_ROWS 3072
 
-/* Status codes. 0 is success; every error is negative and launches nothing. */
+/* Status codes. 0 is success; every error is negative. Every argument error
+ * is found before anything is launched. */
 #define ROUTE_OK 0
 #define ROUTE_E_ARG (-1)    /* NULL pointer, bad abi_version or unknown mode */
 #define ROUTE_E_ROWS (-2)   /* rows outside the mode's envelope, or above the plan's */
@@ -95,7 +97,10 @@ extern "C" {
                                top-16 call on a share plan */
 #define ROUTE_E_ALIGN (-4)  /* a device pointer is not 16-byte aligned */
 #define ROUTE_E_DEVICE (-5) /* no such device, not gfx950, or not the current device */
-#define ROUTE_E_HIP (-6)    /* the HIP runtime rejected a launch */
+#define ROUTE_E_HIP (-6)    /* the HIP runtime rejected one of the call's launches (the
+                               launch's own status, not an error left by earlier
+                               calls); kernels of the call enqueued before it
+                               stay enqueued */
 
 typedef enum { ROUTE_MODE_DECODE = 0, ROUTE_MODE_PREFILL = 1 } route_mode;
 
@@ -123,7 +128,11 @@ int route_prepare(const route_config* cfg, route_plan** out);
 size_t route_workspace_bytes(const route_plan* plan);
 
 /* Latent projection and router logits for `rows` rows (1..plan rows).
- * Every pointer is required. */
+ * Every pointer is required. Prefill plans run the router on three exact BF16
+ * parts of each FP32 weight, then recompute every logit that came out as an
+ * infinity or a NaN (a hidden row holding an infinity or a NaN, or an FP32
+ * partial sum that overflowed) as an exact FP64 dot, so such rows get the
+ * plain dot's IEEE result. */
 int route_latent_router(const route_plan* plan, const void* x, const void* w_latent,
                         const float* w_router, void* latent, float* logits,
                         void* workspace, int32_t rows, void* stream);
@@ -175,6 +184,8 @@ int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t sh
  *     the GEMMs read both operands with 16-byte LDS reads; 89,915,392 bytes.
  *     Every GEMM lane receives the same operand values in the same order as
  *     with [K][N] weights: the results are bitwise those of route_fused.
+ *     (The split is exact for router weights below 2^128 * (1 - 2^-9) in
+ *     magnitude, the largest BF16 value.)
  * Share plans have no packed format: route_packed_weight_bytes returns 0 and
  * the packed calls return ROUTE_E_SHAPE. */
 

@@ -701,11 +701,10 @@ size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off
 }
 
 template <class Sh, bool Packed = false>
-static void launch_shape(const DecodeArgs& a, int rows, hipStream_t stream) {
+static hipError_t launch_shape(const DecodeArgs& a, int rows, hipStream_t stream) {
   if (rows <= 16)
-    hipLaunchKernelGGL((decode_route_kernel<1, Sh, Packed>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_route_kernel<2, Sh, Packed>), dim3(Sh::Grid), dim3(kThreads), 0, stream, a);
+    return launch_kernel(decode_route_kernel<1, Sh, Packed>, dim3(Sh::Grid), dim3(kThreads), stream, a);
+  return launch_kernel(decode_route_kernel<2, Sh, Packed>, dim3(Sh::Grid), dim3(kThreads), stream, a);
 }
 
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
@@ -730,17 +729,11 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (full && packed && rows <= kPackedNarrowMaxRows)
-    launch_shape<PackedShape, true>(a, rows, stream);
-  else if (full && packed)
-    launch_shape<PackedWideShape, true>(a, rows, stream);
-  else if (full)
-    launch_shape<FullShape>(a, rows, stream);
-  else if (n_latent == Tp8Shape::N)
-    launch_shape<Tp8Shape>(a, rows, stream);
-  else
-    launch_shape<Tp16Shape>(a, rows, stream);
-  return hipGetLastError();
+  if (full && packed && rows <= kPackedNarrowMaxRows) return launch_shape<PackedShape, true>(a, rows, stream);
+  if (full && packed) return launch_shape<PackedWideShape, true>(a, rows, stream);
+  if (full) return launch_shape<FullShape>(a, rows, stream);
+  if (n_latent == Tp8Shape::N) return launch_shape<Tp8Shape>(a, rows, stream);
+  return launch_shape<Tp16Shape>(a, rows, stream);
 }
 
 // ------------------------------------------------------------ weight packing --
@@ -810,13 +803,10 @@ hipError_t launch_pack_decode_weights(const uint16_t* w_latent, const float* w_r
                                       hipStream_t stream) {
   uint16_t* lat = static_cast<uint16_t*>(packed);
   float* rt = reinterpret_cast<float*>(static_cast<char*>(packed) + decode_packed_latent_bytes());
-  hipLaunchKernelGGL(pack_latent_kernel, dim3((kPackLatPieces + 255) / 256), dim3(256), 0, stream,
-                     w_latent, lat);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(pack_latent_kernel, dim3((kPackLatPieces + 255) / 256), dim3(256),
+                                     stream, w_latent, lat);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pack_router_kernel, dim3((kPackRtPieces + 255) / 256), dim3(256), 0, stream,
-                     w_router, rt);
-  return hipGetLastError();
+  return launch_kernel(pack_router_kernel, dim3((kPackRtPieces + 255) / 256), dim3(256), stream, w_router, rt);
 }
 
 }  // namespace route

@@ -433,6 +433,111 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     *(u32x4*)(dst + 64 * q) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
 }
 
+// Router logits the GEMM returned as an infinity or a NaN, recomputed exactly.
+//
+// The GEMM multiplies the hidden row by three BF16 parts of each FP32 weight.
+// The parts can differ in sign or be zero, so an infinite hidden value gives
+// inf - inf or inf * 0 (NaN) where the single product x * w is an infinity;
+// and an FP32 chain can overflow where the full float64 dot stays finite. A
+// finite hidden row with no overflow never produces a non-finite logit, and
+// an infinite or NaN hidden value makes every logit of its row non-finite.
+// So every logit the GEMM returned non-finite is recomputed here as a plain
+// FP64 dot of the hidden row with the FP32 weight (rebuilt exactly as
+// hi + mid + lo from the packed parts, each sum exact in FP64), the four
+// K quarters added in a fixed order and rounded once to FP32; finite logits
+// are left as they are. One workgroup per 64 rows x 64 experts: a tile with
+// no non-finite logit (every tile of a finite chunk) only reads its 16 KB of
+// logits and returns.
+constexpr int kFixRows = 64;
+constexpr int kFixExperts = 64;
+
+__device__ __forceinline__ bool f32_nonfinite(float v) {
+  return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u;
+}
+
+template <bool Packed>
+__global__ __launch_bounds__(256) void router_fixup_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           const uint16_t* __restrict__ parts_t,
+                                                           float* __restrict__ logits, int rows) {
+  __shared__ uint64_t bad_rows;      // bit j: row r0 + j has a non-finite logit in this tile
+  __shared__ double red[4][kFixExperts];
+  const int r0 = blockIdx.x * kFixRows;
+  const int e0 = blockIdx.y * kFixExperts;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  // thread t checks row r0 + t / 4, experts e0 + 16 (t % 4) .. + 15
+  const int cr = r0 + (t >> 2);
+  bool bad = false;
+  if (cr < rows) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(logits + (size_t)cr * kExperts + e0 + 16 * (t & 3));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = p[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bad |= f32_nonfinite(v[c]);
+    }
+  }
+  if (t == 0) bad_rows = 0;
+  __syncthreads();
+  const uint64_t m = ballot(bad);    // lanes 4 j .. 4 j + 3 of wave w check row 16 w + j
+  if (lane == 0 && m != 0) {
+    uint64_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((m >> (4 * j)) & 15u) mine |= 1ull << (16 * wave + j);
+    atomicOr((unsigned long long*)&bad_rows, (unsigned long long)mine);
+  }
+  __syncthreads();
+  uint64_t todo = bad_rows;          // the same value in every thread
+  // thread (wave q, lane j): expert e0 + j over K quarter q
+  const int e = e0 + lane;
+  const int kb = wave * (kHidden / 4);
+  while (todo != 0) {
+    const int r = r0 + __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const uint16_t* xr = x + (size_t)r * kHidden;
+    double s = 0.0;
+    if constexpr (Packed) {
+      // the parts of expert e: rows (e / 64) * 192 + 64 p + e % 64 of parts_t
+      const uint16_t* ph = parts_t + (size_t)((e / 64) * 192 + e % 64) * kHidden;
+      for (int k = kb; k < kb + kHidden / 4; k += 8) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + k);
+        const u32x4 hv = *reinterpret_cast<const u32x4*>(ph + k);
+        const u32x4 mv = *reinterpret_cast<const u32x4*>(ph + (size_t)64 * kHidden + k);
+        const u32x4 lv = *reinterpret_cast<const u32x4*>(ph + (size_t)128 * kHidden + k);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int h = i >> 1;
+          auto part = [&](uint32_t pair) { return (double)((i & 1) ? bf16_hi(pair) : bf16_lo(pair)); };
+          const double w = part(hv[h]) + part(mv[h]) + part(lv[h]);
+          s = fma(part(xv[h]), w, s);
+        }
+      }
+    } else {
+#pragma unroll 8
+      for (int k = kb; k < kb + kHidden / 4; ++k)
+        s = fma((double)__uint_as_float((uint32_t)xr[k] << 16), (double)wr[(size_t)k * kExperts + e], s);
+    }
+    red[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0) {
+      float* dst = logits + (size_t)r * kExperts + e;
+      if (f32_nonfinite(*dst)) *dst = (float)(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
+    }
+    __syncthreads();
+  }
+}
+
+static hipError_t launch_router_fixup(const uint16_t* x, const float* wr, const uint16_t* parts_t,
+                                      float* logits, int rows, hipStream_t stream) {
+  const dim3 grid((rows + kFixRows - 1) / kFixRows, kExperts / kFixExperts);
+  return parts_t ? launch_kernel(router_fixup_kernel<true>, grid, dim3(256), stream, x, wr, parts_t, logits, rows)
+                 : launch_kernel(router_fixup_kernel<false>, grid, dim3(256), stream, x, wr, parts_t, logits,
+                                 rows);
+}
+
 // Packing for the K-contiguous GEMM variant, once per weight set, through
 // 32 x 32 LDS tiles: W [7168][3584] -> WT [3584][7168]; Wr [7168][896] ->
 // its three BF16 parts as partsT [2688][7168], part p of expert e in row
@@ -475,13 +580,11 @@ hipError_t launch_pack_prefill_weights(const uint16_t* w_latent, const float* w_
                                        hipStream_t stream) {
   uint16_t* wt = static_cast<uint16_t*>(packed);
   uint16_t* parts_t = reinterpret_cast<uint16_t*>(static_cast<char*>(packed) + prefill_packed_latent_bytes());
-  hipLaunchKernelGGL(pack_prefill_latent_kernel, dim3(kLatent / 32, kHidden / 32), dim3(256), 0, stream,
-                     w_latent, wt);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(pack_prefill_latent_kernel, dim3(kLatent / 32, kHidden / 32), dim3(256),
+                                     stream, w_latent, wt);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pack_prefill_router_kernel, dim3(kExperts / 32, kHidden / 32), dim3(256), 0, stream,
-                     w_router, parts_t);
-  return hipGetLastError();
+  return launch_kernel(pack_prefill_router_kernel, dim3(kExperts / 32, kHidden / 32), dim3(256), stream,
+                       w_router, parts_t);
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -499,9 +602,8 @@ hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, ui
                                  int rows, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
   const int mt = (rows + kGBM - 1) / kGBM;
-  hipLaunchKernelGGL((prefill_gemm_kernel<false, false>), dim3(mt * (kLatent / 224)), dim3(kGThreads), 0,
-                     stream, x, w_latent, (void*)latent, rows, mt);
-  return hipGetLastError();
+  return launch_kernel(prefill_gemm_kernel<false, false>, dim3(mt * (kLatent / 224)), dim3(kGThreads), stream,
+                       x, w_latent, (void*)latent, rows, mt);
 }
 
 hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t* latent, float* logits,
@@ -511,24 +613,26 @@ hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t
   const uint16_t* parts_t =
       reinterpret_cast<const uint16_t*>(static_cast<const char*>(packed) + prefill_packed_latent_bytes());
   const int mt = (rows + kGBM - 1) / kGBM;
-  hipLaunchKernelGGL((prefill_gemm_kernel<false, true>), dim3(mt * (kLatent / 224)), dim3(kGThreads), 0,
-                     stream, x, wt, (void*)latent, rows, mt);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(prefill_gemm_kernel<false, true>, dim3(mt * (kLatent / 224)), dim3(kGThreads),
+                               stream, x, wt, (void*)latent, rows, mt);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_gemm_kernel<true, true>), dim3(mt * (kRouterCols / 192)), dim3(kGThreads), 0,
-                     stream, x, parts_t, (void*)logits, rows, mt);
-  return hipGetLastError();
+  e = launch_kernel(prefill_gemm_kernel<true, true>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
+                    x, parts_t, (void*)logits, rows, mt);
+  if (e != hipSuccess) return e;
+  return launch_router_fixup(x, nullptr, parts_t, logits, rows, stream);
 }
 
 hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
                                  float* logits, int rows, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(router_split_kernel, dim3(kHidden * (kExperts / 8) / 256), dim3(256), 0, stream,
-                     w_router, parts);
+  hipError_t e = launch_kernel(router_split_kernel, dim3(kHidden * (kExperts / 8) / 256), dim3(256), stream,
+                               w_router, parts);
+  if (e != hipSuccess) return e;
   const int mt = (rows + kGBM - 1) / kGBM;
-  hipLaunchKernelGGL((prefill_gemm_kernel<true, false>), dim3(mt * (kRouterCols / 192)), dim3(kGThreads), 0,
-                     stream, x, (const uint16_t*)parts, (void*)logits, rows, mt);
-  return hipGetLastError();
+  e = launch_kernel(prefill_gemm_kernel<true, false>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
+                    x, (const uint16_t*)parts, (void*)logits, rows, mt);
+  if (e != hipSuccess) return e;
+  return launch_router_fixup(x, w_router, nullptr, logits, rows, stream);
 }
 
 }  // namespace route

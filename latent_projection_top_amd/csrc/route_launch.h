@@ -5,7 +5,28 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
 namespace route {
+
+// Enqueue `kernel` on `stream` and return the status of this launch alone.
+// hipLaunchKernel reports what went wrong with the launch itself; reading
+// hipGetLastError() after a launch would instead return (and clear) an error
+// left behind by unrelated earlier calls on the thread. The arguments are
+// converted to the kernel's parameter types and kept alive for the call.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "one argument per kernel parameter");
+  std::tuple<std::decay_t<Params>...> vals{static_cast<std::decay_t<Params>>(args)...};
+  void* ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
+  std::apply([&ptrs](auto&... v) {
+    size_t i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
 
 // Decode workspace: tile counters, then split-K partials, then a logits buffer.
 struct DecodeWorkspace {

@@ -24,9 +24,8 @@ __global__ __launch_bounds__(kWave * kTopkRowsPerBlock) void topk16_kernel(
 hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,
                          hipStream_t stream) {
   const int blocks = (rows + kTopkRowsPerBlock - 1) / kTopkRowsPerBlock;
-  hipLaunchKernelGGL(topk16_kernel, dim3(blocks), dim3(kWave * kTopkRowsPerBlock), 0, stream,
-                     logits, ids, weights, rows);
-  return hipGetLastError();
+  return launch_kernel(topk16_kernel, dim3(blocks), dim3(kWave * kTopkRowsPerBlock), stream, logits, ids,
+                       weights, rows);
 }
 
 }  // namespace route

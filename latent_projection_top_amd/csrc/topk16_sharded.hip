@@ -70,44 +70,47 @@ bool topk16_shards_valid(int shards) {
 }
 
 template <int P>
-static void launch_stage1(const float* logits, uint64_t* cand, int rows, int shards, hipStream_t s) {
+static hipError_t launch_stage1(const float* logits, uint64_t* cand, int rows, int shards, hipStream_t s) {
   const int blocks = (rows * shards + kShardRowsPerBlock - 1) / kShardRowsPerBlock;
-  hipLaunchKernelGGL(topk16_shard_kernel<P>, dim3(blocks), dim3(kWave * kShardRowsPerBlock), 0, s,
-                     logits, cand, rows, shards);
+  return launch_kernel(topk16_shard_kernel<P>, dim3(blocks), dim3(kWave * kShardRowsPerBlock), s, logits,
+                       cand, rows, shards);
 }
 
 template <int Q>
-static void launch_stage2(const uint64_t* cand, int32_t* ids, float* weights, int rows, int shards,
-                          hipStream_t s) {
+static hipError_t launch_stage2(const uint64_t* cand, int32_t* ids, float* weights, int rows, int shards,
+                                hipStream_t s) {
   const int blocks = (rows + kShardRowsPerBlock - 1) / kShardRowsPerBlock;
-  hipLaunchKernelGGL(topk16_merge_kernel<Q>, dim3(blocks), dim3(kWave * kShardRowsPerBlock), 0, s,
-                     cand, ids, weights, rows, shards);
+  return launch_kernel(topk16_merge_kernel<Q>, dim3(blocks), dim3(kWave * kShardRowsPerBlock), s, cand, ids,
+                       weights, rows, shards);
 }
 
 hipError_t launch_topk16_sharded(const float* logits, int shards, int32_t* ids, float* weights,
                                  uint64_t* cand, int rows, hipStream_t stream) {
   if (!topk16_shards_valid(shards) || rows < 1) return hipErrorInvalidValue;
   // keys per lane: stage 1 holds one shard, stage 2 the 16 * shards candidates
+  // both stages' template variants are chosen before anything is launched
   const int p = (kExperts / shards + kWave - 1) / kWave;
-  switch (p) {
-    case 1: launch_stage1<1>(logits, cand, rows, shards, stream); break;
-    case 2: launch_stage1<2>(logits, cand, rows, shards, stream); break;
-    case 4: launch_stage1<4>(logits, cand, rows, shards, stream); break;
-    case 7: launch_stage1<7>(logits, cand, rows, shards, stream); break;
-    case 14: launch_stage1<14>(logits, cand, rows, shards, stream); break;
-    default: return hipErrorInvalidValue;
-  }
   const int q = (kTopK * shards + kWave - 1) / kWave;
-  switch (q) {
-    case 1: launch_stage2<1>(cand, ids, weights, rows, shards, stream); break;
-    case 2: launch_stage2<2>(cand, ids, weights, rows, shards, stream); break;
-    case 4: launch_stage2<4>(cand, ids, weights, rows, shards, stream); break;
-    case 7: launch_stage2<7>(cand, ids, weights, rows, shards, stream); break;
-    case 8: launch_stage2<8>(cand, ids, weights, rows, shards, stream); break;
-    case 14: launch_stage2<14>(cand, ids, weights, rows, shards, stream); break;
-    default: return hipErrorInvalidValue;
+  if ((p != 1 && p != 2 && p != 4 && p != 7 && p != 14) ||
+      (q != 1 && q != 2 && q != 4 && q != 7 && q != 8 && q != 14))
+    return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+  switch (p) {
+    case 1: e = launch_stage1<1>(logits, cand, rows, shards, stream); break;
+    case 2: e = launch_stage1<2>(logits, cand, rows, shards, stream); break;
+    case 4: e = launch_stage1<4>(logits, cand, rows, shards, stream); break;
+    case 7: e = launch_stage1<7>(logits, cand, rows, shards, stream); break;
+    default: e = launch_stage1<14>(logits, cand, rows, shards, stream); break;
   }
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (q) {
+    case 1: return launch_stage2<1>(cand, ids, weights, rows, shards, stream);
+    case 2: return launch_stage2<2>(cand, ids, weights, rows, shards, stream);
+    case 4: return launch_stage2<4>(cand, ids, weights, rows, shards, stream);
+    case 7: return launch_stage2<7>(cand, ids, weights, rows, shards, stream);
+    case 8: return launch_stage2<8>(cand, ids, weights, rows, shards, stream);
+    default: return launch_stage2<14>(cand, ids, weights, rows, shards, stream);
+  }
 }
 
 }  // namespace route

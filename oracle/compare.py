@@ -94,12 +94,18 @@ def logits_check(got, ref, exact, abs_terms, c: float = 1.0) -> dict:
     within = d <= 1
     err = np.abs(got.astype(np.float64) - exact)
     band_ok = err <= 0.5 * f32_spacing(got) + c * U32 * abs_terms
+    large = np.abs(exact) >= 1.0
     return {
         "n": int(d.size),
         "within_1ulp": int(within.sum()),
         "band": int(((~within) & band_ok).sum()),
         "fail": int(((~within) & (~band_ok)).sum()),
         "max_ulp": int(d.max()) if d.size else 0,
+        # ULP distance where the logit is at least 1 in magnitude (the range
+        # the top-16 selects from, where a unit is a fixed fraction of it)
+        "large_n": int(large.sum()),
+        "large_mean_ulp": float(d[large].mean()) if large.any() else 0.0,
+        "large_max_ulp": int(d[large].max()) if large.any() else 0,
         # (outputs whose terms are all zero have no scale and are left out)
         "max_err_over_terms": float((err[abs_terms > 0] / (U32 * abs_terms[abs_terms > 0])).max())
         if (abs_terms > 0).any() else 0.0,

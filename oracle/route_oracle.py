@@ -132,6 +132,13 @@ def logits_exact(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
     return x @ np.asarray(w_router, dtype=np.float32).astype(np.float64)
 
 
+def logits_abs_terms(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """sum_k |x[r, k] * Wr[k, e]| in float64 (the scale of the accumulation
+    error of any FP32 summation order of the logit's terms)."""
+    x = bf16_bits_to_f64(x_bits)
+    return np.abs(x) @ np.abs(np.asarray(w_router, dtype=np.float32).astype(np.float64))
+
+
 def logits_ref(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
     """FP32 router logits, the float64 dot rounded once (nearest-even)."""
     return logits_exact(x_bits, w_router).astype(np.float32)
@@ -139,39 +146,30 @@ def logits_ref(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
 
 # ----------------------------------------------------------- top-16 (a5) --
 
-def _selection_key(logits: np.ndarray) -> np.ndarray:
-    """uint64 key whose descending order is (logit desc, index asc).
+def _rank_order(logits: np.ndarray) -> np.ndarray:
+    """Expert indices of each row sorted by (logit descending, index
+    ascending), with -0.0 equal to +0.0 and NaN after every number.
 
-    The upper 32 bits map the float32 value onto an unsigned order (sign flip
-    for positives, bit inversion for negatives), with -0.0 mapped onto +0.0
-    and NaN onto 0 (below -inf). The lower 32 bits are 0xFFFFFFFF - index, so
-    an equal value with a lower index compares larger. Keys are unique.
+    A plain lexicographic sort on three keys: whether the logit is NaN, the
+    negated logit, the expert index (np.lexsort takes its last key as the
+    primary one).
     """
-    v = np.ascontiguousarray(logits, dtype=np.float32)
-    bits = v.view(np.uint32).astype(np.uint64)
-    neg = (bits >> np.uint64(31)) == 1
-    key = np.where(neg, (~bits) & np.uint64(0xFFFFFFFF), bits | np.uint64(0x80000000))
-    key = np.where(v == 0, np.uint64(0x80000000), key)
-    key = np.where(np.isnan(v), np.uint64(0), key)
-    idx = np.arange(v.shape[-1], dtype=np.uint64)
-    return (key << np.uint64(32)) | (np.uint64(0xFFFFFFFF) - idx)
+    v = np.atleast_2d(np.asarray(logits, dtype=np.float32)).astype(np.float64) + 0.0  # -0.0 -> +0.0
+    nan = np.isnan(v)
+    neg = np.where(nan, 0.0, -v)
+    idx = np.broadcast_to(np.arange(v.shape[-1]), v.shape)
+    return np.lexsort((idx, neg, nan), axis=-1)
 
 
 def topk16_ref(logits: np.ndarray, k: int = TOPK) -> np.ndarray:
     """Standalone top-16 ids per row, int32 [rows, 16], in selection order.
 
     [PR24] "What / why" and "Dependency": the standalone top-16 selects each
-    row's experts from the router logits for rounds of 1..20 rows. The k
-    largest selection keys (see _selection_key) are taken with a library
-    partition, then sorted descending.
+    row's experts from the router logits for rounds of 1..20 rows. The ids are
+    the first k of the full sort of the row's experts by (logit descending,
+    index ascending).
     """
-    logits = np.atleast_2d(logits)
-    e = logits.shape[-1]
-    key = _selection_key(logits)
-    top = np.partition(key, e - k, axis=1)[:, e - k:]
-    top = np.sort(top, axis=1)[:, ::-1]
-    ids = np.uint64(0xFFFFFFFF) - (top & np.uint64(0xFFFFFFFF))
-    return ids.astype(np.int32)
+    return _rank_order(logits)[:, :k].astype(np.int32)
 
 
 def topk16_sharded_ref(logits: np.ndarray, shards: int, k: int = TOPK) -> np.ndarray:
@@ -180,24 +178,21 @@ def topk16_sharded_ref(logits: np.ndarray, shards: int, k: int = TOPK) -> np.nda
 
     [PR24] "What / why": each row keeps its 16 largest experts; [PR265]: the
     router output is split by expert over the ranks (56 experts per rank over
-    16 ranks). Step 1: each of `shards` contiguous expert shards keeps its k
-    largest selection keys (global expert numbering). Step 2: the row's k
-    largest among the k * shards candidates, sorted descending. Both steps use
-    a library partition and sort over the same keys as topk16_ref.
+    16 ranks). Step 1: each of `shards` contiguous expert shards keeps its own
+    top k (topk16_ref on the shard's columns, mapped back to global expert
+    numbers). Step 2: the row's top k among the k * shards candidates, by the
+    same order on (logit, global index).
     """
-    logits = np.atleast_2d(logits)
+    logits = np.atleast_2d(np.asarray(logits, dtype=np.float32))
     rows, e = logits.shape
     if shards < 1 or e % shards or e // shards < k:
         raise ValueError("shards must divide the experts with at least k per shard")
-    key = _selection_key(logits)
     size = e // shards
-    cand = [np.partition(key[:, s * size:(s + 1) * size], size - k, axis=1)[:, size - k:]
-            for s in range(shards)]
-    cand = np.concatenate(cand, axis=1)
-    top = np.partition(cand, cand.shape[1] - k, axis=1)[:, cand.shape[1] - k:]
-    top = np.sort(top, axis=1)[:, ::-1]
-    ids = np.uint64(0xFFFFFFFF) - (top & np.uint64(0xFFFFFFFF))
-    return ids.astype(np.int32)
+    cand = np.concatenate([s * size + topk16_ref(logits[:, s * size:(s + 1) * size], k)
+                           for s in range(shards)], axis=1).astype(np.int64)
+    cand.sort(axis=1)        # global index order, so that ties break on the index
+    vals = np.take_along_axis(logits, cand, axis=1)
+    return np.take_along_axis(cand, _rank_order(vals)[:, :k], axis=1).astype(np.int32)
 
 
 def route_weights_ref(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
@@ -230,6 +225,30 @@ def route_ref_widened(x_bits: np.ndarray, w64: np.ndarray, wr64: np.ndarray) -> 
     ids = topk16_ref(logits)
     return {
         "latent": round_f64_to_bf16_bits(x @ w64),
+        "logits": logits,
+        "ids": ids,
+        "weights": route_weights_ref(logits, ids),
+    }
+
+
+def route_detail_widened(x_bits: np.ndarray, w64: np.ndarray, wr64: np.ndarray) -> dict:
+    """route_ref_widened's outputs plus what the comparators need beside them:
+    the float64 latent and logit dots ("exact", "logits_exact") and the sums
+    of their terms' magnitudes ("abs_terms", "logits_abs_terms"), the same
+    quantities as latent_exact, latent_abs_terms, logits_exact and
+    logits_abs_terms, from weights widened once."""
+    x = bf16_bits_to_f64(x_bits)
+    exact = x @ w64
+    lexact = x @ wr64
+    logits = lexact.astype(np.float32)
+    ids = topk16_ref(logits)
+    ax = np.abs(x)
+    return {
+        "exact": exact,
+        "abs_terms": ax @ np.abs(w64),
+        "logits_exact": lexact,
+        "logits_abs_terms": ax @ np.abs(wr64),
+        "latent": round_f64_to_bf16_bits(exact),
         "logits": logits,
         "ids": ids,
         "weights": route_weights_ref(logits, ids),

@@ -8,6 +8,7 @@ import sys
 import numpy as np
 import torch
 
+from oracle import compare
 from synth import generators as gen
 
 
@@ -37,32 +38,45 @@ def weights_dev(copy: int = 0):
 
 @functools.lru_cache(maxsize=2)
 def weights_f64(copy: int = 0):
-    """Oracle-side float64 views of the weights, converted once per session."""
+    """Oracle-side float64 copies of the weights, widened once per session."""
     from oracle import route_oracle as orc
-    w, wr = weights_host(copy)
-    return orc.bf16_bits_to_f64(w), wr.astype(np.float64)
+    return orc.widen_weights(*weights_host(copy))
 
 
 def oracle_rows(x_bits: np.ndarray, copy: int = 0) -> dict:
-    """Oracle outputs for many rows at once (float64 dots with cached weights).
-    Same arithmetic as oracle.route_ref; the weights are widened once."""
+    """Oracle outputs for many rows at once, with the float64 dots and term
+    magnitudes the comparators need (oracle.route_detail_widened on weights
+    widened once per session)."""
     from oracle import route_oracle as orc
-    w64, wr64 = weights_f64(copy)
-    x64 = orc.bf16_bits_to_f64(x_bits)
-    exact = x64 @ w64
-    lexact = x64 @ wr64
-    logits = lexact.astype(np.float32)
-    ids = orc.topk16_ref(logits)
-    return {
-        "exact": exact,
-        "abs_terms": np.abs(x64) @ np.abs(w64),
-        "logits_exact": lexact,
-        "logits_abs_terms": np.abs(x64) @ np.abs(wr64),
-        "latent": orc.round_f64_to_bf16_bits(exact),
-        "logits": logits,
-        "ids": ids,
-        "weights": orc.route_weights_ref(logits, ids),
-    }
+    return orc.route_detail_widened(x_bits, *weights_f64(copy))
+
+
+def assert_fp64_logits(got, ref, allowance: float = 1e-5) -> None:
+    """Logits the decode route accumulates in FP64 and rounds once: equal to
+    the oracle's correctly rounded FP32 values, except that two float64 sums
+    of the same exact terms in different orders can fall on either side of an
+    FP32 rounding boundary (their difference is about 1e-16 of the sum of the
+    terms' magnitudes against an FP32 unit of about 6e-8 of the logit), so at
+    most 1 ULP and, counted, at most `allowance` of the outputs may differ."""
+    d = compare.f32_ulp_distance(got, ref)
+    off = int((d > 0).sum())
+    assert d.max() <= 1, f"logit {int(d.max())} ULP from the oracle"
+    assert off <= max(2, allowance * d.size), f"{off} of {d.size} logits 1 ULP off"
+
+
+def assert_prefill_logit_error(gc: dict) -> None:
+    """Prefill logits: FP32 MFMA chains of at most 256 K terms folded into
+    FP64. Besides compare.logits_check's pass / fail (every logit within
+    ulp/2 + 2^-24 * sum_k |x_k Wr_k| of the exact dot), three caps set from
+    the measured error of this accumulation (four 3072-row chunks with
+    outliers: largest error 0.59 of 2^-24 * sum_k |x_k Wr_k|, 42 % of the
+    logits more than 1 ULP from the correctly rounded value, mean distance
+    0.99 ULP and largest 15 ULP where |logit| >= 1), each with a margin, so
+    that a longer chain or a lost restart fails (one chain over all 7168 K
+    reaches about 2.5 units)."""
+    assert gc["max_err_over_terms"] <= 0.75, gc
+    assert gc["band"] <= 0.5 * gc["n"], gc
+    assert gc["large_mean_ulp"] <= 1.5 and gc["large_max_ulp"] <= 32, gc
 
 
 class Outputs:

@@ -22,3 +22,36 @@ def test_decode_bytes_formula():
     assert bench.decode_bytes(1) == 77_070_336 + 25_216
     assert bench.decode_bytes(8) == 77_272_064
     assert bench.decode_bytes(20) - bench.decode_bytes(19) == 14_336 + 7_168 + 3_584 + 64 + 64
+
+
+class _StubGraph:
+    def __init__(self, log, count):
+        self.log, self.count = log, count
+
+    def replay(self):
+        self.log.append(self.count)
+
+
+class _StubSetup(bench.DecodeSetup):
+    """DecodeSetup with graphs replaced by counters of the calls they hold."""
+
+    def __init__(self, copies):
+        self.copies = list(range(copies))
+        self.replayed = []
+
+    def capture(self, count=None):
+        return _StubGraph(self.replayed, len(self.copies[:count]))
+
+
+def test_runner_replays_exactly_the_requested_routes():
+    for copies in (1, 3, 8):
+        for steps, warm in ((1600, 80), (20, 5), (7, 0), (8, 8), (1, 1)):
+            d = _StubSetup(copies)
+            run = d.runner([steps, warm])
+            for n in (steps, warm):
+                d.replayed.clear()
+                run(n)
+                assert sum(d.replayed) == n, (copies, n)
+                # whole passes over the copies, then one shorter graph at most
+                assert all(c == copies for c in d.replayed[:n // copies])
+                assert len(d.replayed) == n // copies + (1 if n % copies else 0)

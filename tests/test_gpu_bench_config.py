@@ -20,7 +20,7 @@ import bench
 from oracle import compare
 from oracle import route_oracle as orc
 from synth import generators as gen
-from tests.routekit import bits_host, log, oracle_rows
+from tests.routekit import assert_fp64_logits, assert_prefill_logit_error, bits_host, log, oracle_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -43,11 +43,13 @@ def check(got, ref, tag, logits_ulp=True):
     assert lc["fail"] == 0
     assert lc["rel_rms"] <= 2.0e-3
     if logits_ulp:
-        assert ld.max() <= 2
+        assert_fp64_logits(got["logits"], ref["logits"])
     else:
         gc = compare.logits_check(got["logits"], ref["logits"], ref["logits_exact"],
                                   ref["logits_abs_terms"])
+        log(f"{tag}: logits {gc}")
         assert gc["fail"] == 0, gc
+        assert_prefill_logit_error(gc)
     assert ic["violations"] == 0, ic["bad_rows"][:5]
     assert wc["fail"] == 0
 

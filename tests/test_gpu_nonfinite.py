@@ -7,12 +7,11 @@ the latent row is BF16 +-inf, the logits are FP32 +-inf, the top-16 is the 16
 lowest-indexed experts whose logit is +inf and each weight is exactly 1/16
 (sigmoid(+inf) = 1). With x[r, k] = NaN the whole row is NaN, the top-16 is
 experts 0..15 (NaN orders below -inf, ties go to the lower index) and the
-weights are NaN. The decode route gives exactly these (FP64 sums of the
-partials keep the single infinite term). The prefill router multiplies the
-hidden row by three BF16 parts of each FP32 weight, whose signs can differ,
-so an infinite term there can come out as NaN instead of +-inf: the test
-requires the same non-finite positions as the oracle and a top-16 that is
-the oracle's selection on the logits the call returned."""
+weights are NaN. Both routes must give exactly the oracle's values on such
+rows: the decode route's FP64 sums keep the single infinite term, and the
+prefill route recomputes every logit its GEMM returned non-finite as an exact
+FP64 dot (the GEMM's three BF16 parts of a weight would turn an infinite term
+into inf - inf)."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +19,8 @@ import torch
 from oracle import compare
 from oracle import route_oracle as orc
 from synth import generators as gen
-from tests.routekit import Outputs, bf16_dev, bits_host, log, oracle_rows, weights_dev
+from tests.routekit import (Outputs, assert_fp64_logits, assert_prefill_logit_error, bf16_dev, bits_host, log, oracle_rows,
+                            weights_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,11 +70,12 @@ def check_good_rows(got, ref, good, logits_ulp: bool):
     lc = compare.latent_check(sub["latent"], rsub["latent"], rsub["exact"], rsub["abs_terms"])
     assert lc["fail"] == 0 and lc["rel_rms"] <= 2.0e-3, lc
     if logits_ulp:
-        assert compare.f32_ulp_distance(sub["logits"], rsub["logits"]).max() <= 2
+        assert_fp64_logits(sub["logits"], rsub["logits"])
     else:
         gc = compare.logits_check(sub["logits"], rsub["logits"], rsub["logits_exact"],
                                   rsub["logits_abs_terms"])
         assert gc["fail"] == 0, gc
+        assert_prefill_logit_error(gc)
     ic = compare.ids_check(sub["ids"], rsub["ids"], rsub["logits"])
     assert ic["violations"] == 0, ic["bad_rows"][:5]
     wc = compare.weights_check(sub["weights"], orc.route_weights_ref(sub["logits"], sub["ids"]))
@@ -106,8 +107,9 @@ def test_decode_nonfinite_rows(packed):
         check_good_rows(got, ref, good, logits_ulp=True)
 
 
-def test_prefill_nonfinite_rows():
-    log("prefill with inf / NaN hidden values")
+@pytest.mark.parametrize("packed", [False, True])
+def test_prefill_nonfinite_rows(packed):
+    log(f"prefill with inf / NaN hidden values, packed={packed}")
     w, wr = weights_dev(0)
     rows = 96
     xs, bad = poisoned_rows(rows, bank=700)
@@ -115,12 +117,40 @@ def test_prefill_nonfinite_rows():
     ws = plan.new_workspace()
     o = Outputs(rows)
     o.poison()
-    route.fused(plan, bf16_dev(xs), w, wr, o.latent, o.logits, o.ids, o.weights, ws)
+    if packed:
+        pk = route.pack_weights(plan, w, wr)
+        route.fused_packed(plan, bf16_dev(xs), pk, o.latent, o.logits, o.ids, o.weights, ws)
+    else:
+        route.fused(plan, bf16_dev(xs), w, wr, o.latent, o.logits, o.ids, o.weights, ws)
     torch.cuda.synchronize()
     got = {"latent": bits_host(o.latent), "logits": o.logits.cpu().numpy(),
            "ids": o.ids.cpu().numpy(), "weights": o.weights.cpu().numpy()}
     with np.errstate(invalid="ignore", over="ignore"):
         ref = oracle_rows(xs)
-    check_bad_rows(got, ref, bad, exact_logits=False)
+    check_bad_rows(got, ref, bad, exact_logits=True)
     good = np.array([r for r in range(rows) if r not in bad])
     check_good_rows(got, ref, good, logits_ulp=False)
+
+
+def test_prefill_nonfinite_latent_router_two_tiles():
+    """route_latent_router alone (no top-16) on a 200-row chunk whose bad rows
+    sit in two 64-row blocks of the recompute and two 192-row GEMM tiles: the
+    same exact logits as the fused call."""
+    log("prefill latent_router with inf / NaN hidden values, 200 rows")
+    w, wr = weights_dev(0)
+    rows = 200
+    xs, bad = poisoned_rows(rows, bank=701)
+    plan = route.Plan(route.MODE_PREFILL, rows)
+    ws = plan.new_workspace()
+    o = Outputs(rows)
+    o.poison()
+    route.latent_router(plan, bf16_dev(xs), w, wr, o.latent, o.logits, ws)
+    torch.cuda.synchronize()
+    g = o.logits.cpu().numpy()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle_rows(xs)
+    for r in bad:
+        e = ref["logits"][r]
+        assert np.array_equal(np.isnan(g[r]), np.isnan(e)), r
+        assert np.array_equal(g[r][~np.isnan(e)], e[~np.isnan(e)]), r
+    assert np.isfinite(np.delete(g, bad, axis=0)).all()

@@ -12,7 +12,7 @@ import torch
 from oracle import compare
 from oracle import route_oracle as orc
 from synth import generators as gen
-from tests.routekit import Outputs, bf16_dev, log, oracle_rows, weights_dev
+from tests.routekit import Outputs, assert_prefill_logit_error, bf16_dev, log, oracle_rows, weights_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,7 @@ def check_outputs(xs, got, tag):
     assert lc["rel_rms"] <= 2.0e-3
     assert lc["band"] <= max(4, 1e-4 * lc["n"])
     assert gc["fail"] == 0
+    assert_prefill_logit_error(gc)
     assert ic["violations"] == 0, ic["bad_rows"][:5]
     assert wc["fail"] == 0 and wc2["fail"] == 0
 

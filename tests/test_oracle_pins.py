@@ -428,3 +428,133 @@ def test_route_ref_widened_matches_parts():
     assert np.array_equal(a["latent"], o.latent_ref(x, w))
     assert np.array_equal(a["logits"], o.logits_ref(x, wr))
     assert np.array_equal(a["ids"], o.topk16_ref(o.logits_ref(x, wr)))
+
+
+# ------------------------------------------- error scales and comparators --
+
+@pytest.mark.parametrize("k", [3, 16, 64])
+def test_abs_terms_against_rational_sums(k):
+    """latent_abs_terms / logits_abs_terms are sum_k |x_k w_k| (not |sum_k x_k
+    w_k|, not sum |x| * sum |w|): checked against exact rational sums, on rows
+    built so that the signed sum cancels to exactly zero."""
+    r = np.random.default_rng(100 + k)
+    x = to_bits(r.standard_normal((3, k)) * np.exp2(r.integers(-4, 4, (3, k))))
+    w = to_bits(r.standard_normal((k, 6)) * 0.05)
+    wr = (r.standard_normal((k, 5)) * 0.05).astype(np.float32)
+    # row 2: x = (a, a, ...) against a column whose two halves cancel
+    half = k // 2
+    x[2, :] = x[2, 0]
+    w[half:2 * half, 5] = w[:half, 5] ^ np.uint16(0x8000)
+    w[2 * half:, 5] = 0
+    wr[half:2 * half, 4] = -wr[:half, 4]
+    wr[2 * half:, 4] = 0
+    xf, wf = o.bf16_bits_to_f64(x), o.bf16_bits_to_f64(w)
+    lat, lgt = o.latent_abs_terms(x, w), o.logits_abs_terms(x, wr)
+    for i in range(3):
+        for n in range(6):
+            want = sum(abs(Fraction(xf[i, j]) * Fraction(wf[j, n])) for j in range(k))
+            assert abs(Fraction(lat[i, n]) - want) <= want * k * Fraction(2) ** -52
+        for e in range(5):
+            want = sum(abs(Fraction(xf[i, j]) * Fraction(float(wr[j, e]))) for j in range(k))
+            assert abs(Fraction(lgt[i, e]) - want) <= want * k * Fraction(2) ** -52
+    # the cancelling column: the signed dot is zero, the magnitudes are not
+    assert o.latent_exact(x, w)[2, 5] == 0.0 and lat[2, 5] > 0.0
+    assert o.logits_exact(x, wr)[2, 4] == 0.0 and lgt[2, 4] > 0.0
+
+
+def _logits_case(err_units):
+    """One logit whose float64 value is exact = 2^-10 (f32 unit 2^-33), with
+    sum |terms| = 64 (so 2^-24 * 64 = 2^-18), and a returned value
+    err_units * (ulp/2 + 2^-18) above it."""
+    exact = np.array([2.0 ** -10])
+    terms = np.array([64.0])
+    ref = exact.astype(np.float32)
+    bound = 0.5 * 2.0 ** -33 + 2.0 ** -18
+    got = np.array([exact[0] + err_units * bound], dtype=np.float32)
+    return got, ref, exact, terms
+
+
+def test_logits_check_band_edges():
+    # within 1 ULP: passes as within
+    got, ref, exact, terms = _logits_case(0.0)
+    near = np.nextafter(ref, np.float32(1))
+    r = c.logits_check(near, ref, exact, terms)
+    assert r["within_1ulp"] == 1 and r["fail"] == 0
+    # far more than 1 ULP off but inside ulp/2 + 2^-24 sum|terms|: a band output
+    got, ref, exact, terms = _logits_case(0.9)
+    r = c.logits_check(got, ref, exact, terms)
+    assert r["within_1ulp"] == 0 and r["band"] == 1 and r["fail"] == 0
+    assert 0.85 <= r["max_err_over_terms"] <= 0.95
+    # just outside the bound: fails (a unit of 2^-23 instead of 2^-24, or a
+    # factor c of 2, would let it pass)
+    got, ref, exact, terms = _logits_case(1.1)
+    r = c.logits_check(got, ref, exact, terms)
+    assert r["fail"] == 1 and r["band"] == 0
+    # c scales the band: c = 2 admits the same value, c = 0.5 rejects 0.9
+    assert c.logits_check(got, ref, exact, terms, c=2.0)["fail"] == 0
+    got, ref, exact, terms = _logits_case(0.9)
+    assert c.logits_check(got, ref, exact, terms, c=0.5)["fail"] == 1
+
+
+def test_logits_check_without_terms_needs_half_ulp():
+    # no terms (sum |terms| = 0): only ulp(got)/2 is allowed, and 2 ULPs fail
+    exact = np.array([1.0 + 2.0 ** -24])     # halfway between 1 and 1 + 2^-23
+    ref = np.array([1.0], dtype=np.float32)   # ties to even
+    up = np.nextafter(np.float32(1.0), np.float32(2))
+    assert c.logits_check(np.array([up]), ref, exact, np.zeros(1))["fail"] == 0
+    up2 = np.nextafter(up, np.float32(2))
+    up3 = np.nextafter(up2, np.float32(2))
+    assert c.logits_check(np.array([up3]), ref, exact, np.zeros(1))["fail"] == 1
+
+
+def test_latent_check_band_edges():
+    # exact = 2^-6, BF16 unit there 2^-13; sum |terms| = 2^14 gives a band of
+    # ulp/2 + 2^-10; 3 BF16 units off (3 * 2^-13 < 2^-10) is a band output,
+    # 12 units off (12 * 2^-13 > 2^-14 + 2^-10) fails
+    exact = np.array([2.0 ** -6])
+    ref = o.round_f64_to_bf16_bits(exact)
+    terms = np.array([2.0 ** 14])
+    r = c.latent_check(ref + np.uint16(3), ref, exact, terms)
+    assert r["band"] == 1 and r["fail"] == 0
+    r = c.latent_check(ref + np.uint16(12), ref, exact, terms)
+    assert r["fail"] == 1
+
+
+def test_route_detail_equals_plain_parts():
+    x = g.hidden(4, bank=12)
+    w, wr = g.latent_weight(0), g.router_weight(0)
+    d = o.route_detail_widened(x, *o.widen_weights(w, wr))
+    ref = o.route_ref(x, w, wr)
+    for key in ("latent", "logits", "ids", "weights"):
+        assert np.array_equal(d[key], ref[key]), key
+    assert np.array_equal(d["exact"], o.latent_exact(x, w))
+    assert np.array_equal(d["abs_terms"], o.latent_abs_terms(x, w))
+    assert np.array_equal(d["logits_exact"], o.logits_exact(x, wr))
+    assert np.array_equal(d["logits_abs_terms"], o.logits_abs_terms(x, wr))
+
+
+def test_gpu_tests_oracle_rows_equal_route_ref():
+    """The helper every GPU parity test compares against (tests/routekit.py)
+    returns the oracle's route."""
+    from tests.routekit import oracle_rows
+    w, wr = g.latent_weight(0), g.router_weight(0)
+    for bank, rows in ((0, 1), (1, 8), (2, 20)):
+        x = g.hidden(rows, bank=bank)
+        got = oracle_rows(x)
+        ref = o.route_ref(x, w, wr)
+        for key in ("latent", "logits", "ids", "weights"):
+            assert np.array_equal(got[key], ref[key]), (bank, key)
+        assert np.array_equal(got["abs_terms"], o.latent_abs_terms(x, w))
+        assert np.array_equal(got["logits_abs_terms"], o.logits_abs_terms(x, wr))
+
+
+def test_logits_check_large_logit_statistics():
+    # |exact| >= 1 only: 2.0 (got 3 ULP above) and -1.5 (exact); 0.25 is left out
+    exact = np.array([2.0, -1.5, 0.25])
+    ref = exact.astype(np.float32)
+    got = ref.copy()
+    for _ in range(3):
+        got[0] = np.nextafter(got[0], np.float32(3))
+    got[2] = np.nextafter(got[2], np.float32(1))
+    r = c.logits_check(got, ref, exact, np.full(3, 1e6))
+    assert r["large_n"] == 2 and r["large_max_ulp"] == 3 and r["large_mean_ulp"] == 1.5
