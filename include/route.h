@@ -101,6 +101,8 @@ extern "C" {
                                launch's own status, not an error left by earlier
                                calls); kernels of the call enqueued before it
                                stay enqueued */
+#define ROUTE_E_SCRATCH (-7) /* route_fused_packed_noalloc: the call needs more than
+                                the library's static scratch holds */
 
 typedef enum { ROUTE_MODE_DECODE = 0, ROUTE_MODE_PREFILL = 1 } route_mode;
 
@@ -210,6 +212,27 @@ int route_latent_router_packed(const route_plan* plan, const void* x, const void
 int route_fused_packed(const route_plan* plan, const void* x, const void* packed, void* latent,
                        float* logits, int32_t* ids, float* weights, void* workspace, int32_t rows,
                        void* stream);
+
+/* route_fused_packed without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). It allocates nothing and calls no allocating
+ * routine: its scratch is a static device array inside the library, one per
+ * GPU, ROUTE_STATIC_SCRATCH_BYTES bytes, held until the process ends; its
+ * address is taken and the array cleared when the first plan for the device
+ * is prepared. Decode plans (whole route, 1..20 rows) keep their counters and
+ * split-K partials there, and their logits when `logits` is NULL; prefill
+ * plans use it only for the logits when `logits` is NULL, at most
+ * ROUTE_STATIC_SCRATCH_BYTES - 512 bytes (rows * 3584 bytes), and return
+ * ROUTE_E_SCRATCH above that. Outputs are bitwise those of route_fused_packed
+ * on the same plan. Every call on a GPU shares that GPU's array, and the
+ * decode counters carry over from call to call: two calls that overlap in
+ * time on one GPU (different streams, threads or graphs running at once)
+ * race on it and must not be issued. Other statuses as route_fused_packed;
+ * ROUTE_E_HIP if the array's address could not be taken for the device. */
+#define ROUTE_STATIC_SCRATCH_BYTES 3512832u
+int route_fused_packed_noalloc(const route_plan* plan, const void* x, const void* packed, void* latent,
+                               float* logits, int32_t* ids, float* weights, int32_t rows,
+                               void* stream);
 
 /* Free a plan (NULL is accepted). */
 void route_destroy(route_plan* plan);

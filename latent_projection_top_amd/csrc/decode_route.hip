@@ -44,8 +44,11 @@
 // weights and the BF16 hidden values widened exactly to FP64 (rows 16..19 as
 // FP64 FMAs on the VALU), so the logits are accumulated in FP64 end to end and
 // rounded to FP32 once.
+#include "route.h"
 #include "route_device.h"
 #include "route_launch.h"
+
+#include <mutex>
 
 namespace route {
 
@@ -145,6 +148,7 @@ constexpr int router_depth() {
 using Tp8Shape = DecodeShape<448, 112, 7, 28>;
 using Tp16Shape = DecodeShape<224, 56, 14, 28>;
 constexpr int kDecodeCounters = FullShape::Counters;   // the largest counter set
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters &&
                   PackedShape::Counters == kDecodeCounters && PackedWideShape::Counters == kDecodeCounters,
               "every shape's counters fit the workspace's counter area");
@@ -660,8 +664,6 @@ void decode_route_kernel(DecodeArgs a) {
   }
 }
 
-static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
 // Sh2: a second shape sharing the workspace (the whole route's packed
 // launches share the [K][N] launch's counters and partial areas); each
 // partial area fits the larger of the two.
@@ -735,6 +737,78 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   if (n_latent == Tp8Shape::N) return launch_shape<Tp8Shape>(a, rows, stream);
   return launch_shape<Tp16Shape>(a, rows, stream);
 }
+
+// ----------------------------------------------------- static device scratch --
+//
+// Scratch of the allocation-free entry point (route_fused_packed_noalloc),
+// for callers that cannot allocate device memory: this code object's device
+// global, one copy per GPU, held until the process ends. Layout for the
+// packed launches at up to 20 decode rows: the counter area, the latent
+// partials [8 splits][20][3584] FP32, the router partials [8 splits][20][896]
+// FP64, then a logits buffer [20][896] FP32. Every call on a GPU shares its
+// copy; the decode kernels leave the counters in the state the next call
+// expects, so it is cleared once, when the first plan for the device is
+// prepared. The kernels receive its address, never the array's name (in
+// host code the name is a host-side stand-in, not a device address).
+constexpr size_t kStaticOffLat = align256(sizeof(uint32_t) * kDecodeCounters);
+constexpr size_t kStaticOffRt =
+    kStaticOffLat + align256(sizeof(float) * PackedShape::SplitsL * kDecodeMaxRows * kLatent);
+constexpr size_t kStaticOffLogits =
+    kStaticOffRt + align256(sizeof(double) * PackedShape::SplitsR * kDecodeMaxRows * kExperts);
+constexpr size_t kStaticBytes = kStaticOffLogits + align256(sizeof(float) * kDecodeMaxRows * kExperts);
+static_assert(PackedWideShape::SplitsL <= PackedShape::SplitsL &&
+                  PackedWideShape::SplitsR <= PackedShape::SplitsR,
+              "both packed launches fit the static partial areas");
+
+static_assert(kStaticBytes == ROUTE_STATIC_SCRATCH_BYTES, "the size the header states");
+
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch_init(int device) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (g_static_ptr[device] != nullptr) return hipSuccess;
+  int prev = -1;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return e;
+  if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  // cleared once (the decode counters must start at zero), before any call
+  // on this device can use it
+  if (e == hipSuccess) e = hipMemset(p, 0, kStaticBytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) g_static_ptr[device] = p;
+  if (prev != device) {
+    const hipError_t r = hipSetDevice(prev);
+    if (e == hipSuccess) e = r;
+  }
+  return e;
+}
+
+void* static_scratch(int device, size_t* bytes) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  *bytes = kStaticBytes;
+  return device >= 0 && device < kMaxDevices ? g_static_ptr[device] : nullptr;
+}
+
+DecodeWorkspace static_decode_workspace(void* base, float** logits) {
+  char* b = static_cast<char*>(base);
+  DecodeWorkspace d;
+  d.counters = reinterpret_cast<uint32_t*>(b);
+  d.lat_part = reinterpret_cast<float*>(b + kStaticOffLat);
+  d.rt_part = reinterpret_cast<double*>(b + kStaticOffRt);
+  *logits = reinterpret_cast<float*>(b + kStaticOffLogits);
+  return d;
+}
+
+size_t static_free_offset() { return kStaticOffLat; }
 
 // ------------------------------------------------------------ weight packing --
 //

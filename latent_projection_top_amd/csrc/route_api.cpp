@@ -124,6 +124,11 @@ int route_prepare(const route_config* cfg, route_plan** out) {
   if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) return ROUTE_E_DEVICE;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return ROUTE_E_DEVICE;
 
+  // the allocation-free entry point's static scratch: its device address is
+  // taken (and the array cleared) once per device, here, with the device
+  // current; a failure only disables that entry point on the device
+  (void)route::static_scratch_init(cfg->device);
+
   route_plan* p = new (std::nothrow) route_plan();
   if (p == nullptr) return ROUTE_E_ARG;
   p->mode = cfg->mode;
@@ -245,6 +250,39 @@ int route_fused_packed(const route_plan* plan, const void* x, const void* packed
                            rows, true, static_cast<hipStream_t>(stream), true);
 }
 
+int route_fused_packed_noalloc(const route_plan* plan, const void* x, const void* packed, void* latent,
+                               float* logits, int32_t* ids, float* weights, int32_t rows, void* stream) {
+  if (!plan || !x || !packed || !latent || !ids || !weights) return ROUTE_E_ARG;
+  if (!packed_plan(plan)) return ROUTE_E_SHAPE;
+  if (int st = check_rows(plan, rows)) return st;
+  if (misaligned(x) || misaligned(packed) || misaligned(latent) || (logits && misaligned(logits)) ||
+      misaligned(ids) || misaligned(weights))
+    return ROUTE_E_ALIGN;
+  if (int st = check_device(plan)) return st;
+  size_t cap = 0;
+  void* scratch = route::static_scratch(plan->device, &cap);
+  if (scratch == nullptr) return ROUTE_E_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan->mode == ROUTE_MODE_DECODE) {
+    float* lg_buf = nullptr;
+    const route::DecodeWorkspace ws = route::static_decode_workspace(scratch, &lg_buf);
+    // the static partial areas are laid out for ROUTE_DECODE_MAX_ROWS rows
+    return status_of(route::launch_decode_route(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(packed), packed_router(plan, packed),
+        static_cast<uint16_t*>(latent), logits ? logits : lg_buf, ids, weights, ws, rows,
+        ROUTE_DECODE_MAX_ROWS, plan->latent, plan->experts, true, true, s));
+  }
+  // prefill: the scratch holds the logits only when the caller passes none,
+  // past the decode counters
+  float* lg = logits;
+  if (lg == nullptr) {
+    const size_t off = route::static_free_offset();
+    if ((size_t)rows * ROUTE_EXPERTS * sizeof(float) > cap - off) return ROUTE_E_SCRATCH;
+    lg = reinterpret_cast<float*>(static_cast<char*>(scratch) + off);
+  }
+  return run_prefill_packed(x, packed, latent, lg, ids, weights, rows, true, s);
+}
+
 void route_destroy(route_plan* plan) { delete plan; }
 
 const char* route_strerror(int status) {
@@ -258,6 +296,9 @@ const char* route_strerror(int status) {
     case ROUTE_E_ALIGN: return "device pointer not 16-byte aligned";
     case ROUTE_E_DEVICE: return "device missing, not gfx950, or not the current device";
     case ROUTE_E_HIP: return "HIP launch failed";
+    case ROUTE_E_SCRATCH:
+      return "the call needs more device scratch than the library's static scratch holds (pass "
+             "logits, or call route_fused_packed with a workspace)";
     default: return "unknown status";
   }
 }

@@ -55,6 +55,18 @@ size_t decode_packed_bytes();
 hipError_t launch_pack_decode_weights(const uint16_t* w_latent, const float* w_router, void* packed,
                                       hipStream_t stream);
 
+// Static device scratch of the allocation-free entry point (one per GPU).
+// static_scratch_init takes the array's device address on `device` (made
+// current for the call) and clears it, once per device; static_scratch
+// returns that address (nullptr before a successful init) and its size.
+// static_decode_workspace lays a decode workspace for up to 20 rows of the
+// packed launches over it, with a logits buffer; from static_free_offset on,
+// the array holds nothing a later call needs (partials and logits only).
+hipError_t static_scratch_init(int device);
+void* static_scratch(int device, size_t* bytes);
+DecodeWorkspace static_decode_workspace(void* base, float** logits);
+size_t static_free_offset();
+
 hipError_t launch_topk16(const float* logits, int32_t* ids, float* weights, int rows,
                          hipStream_t stream);
 

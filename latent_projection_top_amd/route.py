@@ -34,12 +34,15 @@ E_SHAPE = -3
 E_ALIGN = -4
 E_DEVICE = -5
 E_HIP = -6
+E_SCRATCH = -7
+STATIC_SCRATCH_BYTES = 3512832
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libroute.so")
 
 SYMBOLS = ("route_prepare", "route_workspace_bytes", "route_latent_router", "route_topk16",
            "route_fused", "route_topk16_sharded", "route_packed_weight_bytes", "route_pack_weights",
-           "route_latent_router_packed", "route_fused_packed", "route_destroy", "route_strerror")
+           "route_latent_router_packed", "route_fused_packed", "route_fused_packed_noalloc",
+           "route_destroy", "route_strerror")
 
 
 class RouteError(RuntimeError):
@@ -80,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.route_latent_router_packed.restype = ctypes.c_int
     lib.route_fused_packed.argtypes = [vp, vp, vp, vp, f32p, i32p, f32p, vp, i32, vp]
     lib.route_fused_packed.restype = ctypes.c_int
+    lib.route_fused_packed_noalloc.argtypes = [vp, vp, vp, vp, f32p, i32p, f32p, i32, vp]
+    lib.route_fused_packed_noalloc.restype = ctypes.c_int
     lib.route_destroy.argtypes = [vp]
     lib.route_destroy.restype = None
     lib.route_strerror.argtypes = [ctypes.c_int]
@@ -292,3 +297,23 @@ def fused_packed(plan: Plan, x, packed, latent, logits, ids, weights, workspace,
         int(rows), _stream(stream))
     if st != OK:
         raise RouteError(st, "route_fused_packed")
+
+
+def fused_packed_noalloc(plan: Plan, x, packed, latent, logits, ids, weights, rows: int | None = None,
+                         stream=None) -> None:
+    """route_fused_packed_noalloc: the fused route on packed weights with the
+    library's static device scratch instead of a workspace (nothing is
+    allocated). `logits` may be None. Calls that overlap in time on one GPU
+    race on that scratch."""
+    rows = x.shape[0] if rows is None else rows
+    st = LIB.route_fused_packed_noalloc(
+        ctypes.c_void_p(plan.handle),
+        _ptr(x, torch.bfloat16, (rows, HIDDEN), "x", plan.device),
+        _packed_ptr(plan, packed),
+        _ptr(latent, torch.bfloat16, (rows, LATENT), "latent", plan.device),
+        _ptr(logits, torch.float32, (rows, EXPERTS), "logits", plan.device),
+        _ptr(ids, torch.int32, (rows, TOPK), "ids", plan.device),
+        _ptr(weights, torch.float32, (rows, TOPK), "weights", plan.device),
+        int(rows), _stream(stream))
+    if st != OK:
+        raise RouteError(st, "route_fused_packed_noalloc")

@@ -75,6 +75,8 @@ int main(void) {
          "route_latent_router_packed without a plan");
   expect(route_fused_packed(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, NULL), ROUTE_E_ARG,
          "route_fused_packed without a plan");
+  expect(route_fused_packed_noalloc(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, NULL), ROUTE_E_ARG,
+         "route_fused_packed_noalloc without a plan");
   if (route_workspace_bytes(NULL) != 0 || route_packed_weight_bytes(NULL) != 0) {
     printf("FAIL sizes of a NULL plan are not 0\n");
     ++failures;
@@ -83,7 +85,7 @@ int main(void) {
 
   {
     const int codes[] = {ROUTE_OK, ROUTE_E_ARG, ROUTE_E_ROWS, ROUTE_E_SHAPE,
-                         ROUTE_E_ALIGN, ROUTE_E_DEVICE, ROUTE_E_HIP};
+                         ROUTE_E_ALIGN, ROUTE_E_DEVICE, ROUTE_E_HIP, ROUTE_E_SCRATCH};
     const int n = (int)(sizeof codes / sizeof codes[0]);
     int i, j;
     for (i = 0; i < n; ++i) {

@@ -45,8 +45,9 @@ def test_binding_constants_match_header():
     assert d["ROUTE_DECODE_MAX_ROWS"] == route.DECODE_MAX_ROWS == FACTS["decode_rows_accepted"]["max"]
     assert d["ROUTE_PREFILL_MAX_ROWS"] == route.PREFILL_MAX_ROWS == FACTS["prefill_chunk_rows"]["value"]
     assert d["ROUTE_ABI_VERSION"] == route.ABI_VERSION
-    for k in ("OK", "E_ARG", "E_ROWS", "E_SHAPE", "E_ALIGN", "E_DEVICE", "E_HIP"):
+    for k in ("OK", "E_ARG", "E_ROWS", "E_SHAPE", "E_ALIGN", "E_DEVICE", "E_HIP", "E_SCRATCH"):
         assert d["ROUTE_" + k] == getattr(route, k)
+    assert d["ROUTE_STATIC_SCRATCH_BYTES"] == route.STATIC_SCRATCH_BYTES
 
 
 def test_experts_match_page_shards():
@@ -56,8 +57,8 @@ def test_experts_match_page_shards():
 
 
 def test_strerror_distinct():
-    msgs = {route.strerror(s) for s in (0, -1, -2, -3, -4, -5, -6)}
-    assert len(msgs) == 7
+    msgs = {route.strerror(s) for s in (0, -1, -2, -3, -4, -5, -6, -7)}
+    assert len(msgs) == 8
     assert route.strerror(-99) == "unknown status"
 
 
@@ -172,6 +173,7 @@ def test_run_calls_reject_null_plan():
     assert route.LIB.route_pack_weights(None, None, None, None, None) == route.E_ARG
     assert route.LIB.route_latent_router_packed(None, None, None, None, None, None, 1, None) == route.E_ARG
     assert route.LIB.route_fused_packed(None, None, None, None, None, None, None, None, 1, None) == route.E_ARG
+    assert route.LIB.route_fused_packed_noalloc(None, None, None, None, None, None, None, 1, None) == route.E_ARG
     route.LIB.route_destroy(None)
 
 
