@@ -1,16 +1,16 @@
 """Graph-replay stress and the cancelling-partials accuracy set on the GPU.
 
-Stress (page "Optionally gather the Kimi3 prefill latent instead of reducing
-it", Tests: CUDA-graph replays with a new input bank every replay and outputs
-poisoned inside the graph, 0 mismatches): route_fused is captured in a HIP
-graph once; every replay takes a new bank, the outputs are poisoned inside the
-graph before the route runs, and each replay must equal the eager result for
-its bank. The workspace counters must be back in their idle state afterwards.
+Stress, modelled on the graph-replay check of page "Optionally gather the
+Kimi3 prefill latent instead of reducing it" (Tests): route_fused is captured
+in a HIP graph once; every replay takes a new bank, the outputs are poisoned
+inside the graph before the route runs, and each replay must equal the eager
+result for its bank. The workspace counters must be back in their idle state
+afterwards.
 
-Cancelling set (same page, Description, numerics bullet: on cancelling partials
-one rounding keeps its accuracy while per-shard rounding loses it): 1024 rows
-whose two halves of K cancel; relative RMS of the latent against float64 stays
-<= 2.0e-3 through the decode and the prefill kernels."""
+Cancelling set (same page, Description, numerics bullet, which compares the
+two accuracies on partials that cancel): 1024 rows whose two halves of K
+cancel; relative RMS of the latent against float64 stays <= 2.0e-3 through
+the decode and the prefill kernels."""
 import numpy as np
 import pytest
 import torch
