@@ -524,7 +524,8 @@ def main():
             "mfma_work_frac": round(mfma_flops / (t_lr * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "flops_note": "method: 2*M*K*(3584+896) = 197.3 GFLOP; MFMA work: the router runs on three "
                           "exact BF16 parts of its FP32 weight, 276.2 GFLOP; both over latent_router_us "
-                          "(the two GEMMs and the non-finite logit check); per-kernel times are in "
+                          "(the two GEMMs; the router GEMM also recomputes any non-finite logit); per-kernel "
+                          "times are in "
                           "profiles/prefill_gemm_3072_kernel_trace.md",
             "router_variant": "FP32 weight split into 3 exact BF16 parts, BF16 MFMA, FP32 chains "
                               "restarted every 256 K and folded into FP64",

@@ -141,12 +141,92 @@ __device__ __forceinline__ s16x4 lds_tr16(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
 }
 
+__device__ __forceinline__ bool f32_nonfinite(float v) {
+  return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u;
+}
+
+// Router logits the GEMM returned as an infinity or a NaN, recomputed exactly
+// by the workgroup that computed them.
+//
+// The GEMM multiplies the hidden row by three BF16 parts of each FP32 weight.
+// The parts can differ in sign or be zero, so an infinite hidden value gives
+// inf - inf or inf * 0 (NaN) where the single product x * w is an infinity;
+// and an FP32 chain can overflow where the full float64 dot stays finite. A
+// finite hidden row with no overflow never produces a non-finite logit, and
+// an infinite or NaN hidden value makes every logit of its row non-finite.
+// So every logit of the block's tile that came out non-finite is recomputed
+// as a plain FP64 dot of the hidden row with the FP32 weight, rebuilt exactly
+// as hi + mid + lo from the parts (each sum exact in FP64): waves 0..3 take
+// one K quarter each for the tile's 64 experts, the four quarters are added
+// in a fixed order and rounded once to FP32; finite logits keep the GEMM's
+// value. mask[b] bit j: row bm0 + 64 b + j holds a non-finite logit of the
+// tile. red: 256 doubles of LDS.
+template <bool BT>
+__device__ void router_recompute(const uint16_t* __restrict__ x, const uint16_t* __restrict__ parts,
+                                 float* __restrict__ logits, int bm0, int group, const uint64_t (&mask)[kGBM / 64],
+                                 double* red) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int e = group * 64 + lane;
+  const int kb = (wave & 3) * (kHidden / 4);
+#pragma unroll 1
+  for (int b = 0; b < kGBM / 64; ++b) {
+    uint64_t todo = mask[b];
+    while (todo != 0) {
+      const int r = bm0 + 64 * b + __builtin_ctzll(todo);
+      todo &= todo - 1;
+      if (wave < 4) {
+        const uint16_t* xr = x + (size_t)r * kHidden;
+        double s = 0.0;
+        if constexpr (BT) {
+          // part p of expert e: row group * 192 + 64 p + lane of [2688][7168]
+          const uint16_t* ph = parts + (size_t)(group * 192 + lane) * kHidden;
+          for (int k = kb; k < kb + kHidden / 4; k += 8) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + k);
+            const u32x4 hv = *reinterpret_cast<const u32x4*>(ph + k);
+            const u32x4 mv = *reinterpret_cast<const u32x4*>(ph + (size_t)64 * kHidden + k);
+            const u32x4 lv = *reinterpret_cast<const u32x4*>(ph + (size_t)128 * kHidden + k);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int h = i >> 1;
+              auto part = [&](uint32_t pair) { return (double)((i & 1) ? bf16_hi(pair) : bf16_lo(pair)); };
+              const double w = part(hv[h]) + part(mv[h]) + part(lv[h]);
+              s = fma(part(xv[h]), w, s);
+            }
+          }
+        } else {
+          // part p of expert e at [k][group * 192 + 64 p + lane] of [7168][2688]
+          const uint16_t* pk = parts + group * 192 + lane;
+#pragma unroll 8
+          for (int k = kb; k < kb + kHidden / 4; ++k) {
+            const uint16_t* q = pk + (size_t)k * kRouterCols;
+            const double w = (double)__uint_as_float((uint32_t)q[0] << 16) +
+                             (double)__uint_as_float((uint32_t)q[64] << 16) +
+                             (double)__uint_as_float((uint32_t)q[128] << 16);
+            s = fma((double)__uint_as_float((uint32_t)xr[k] << 16), w, s);
+          }
+        }
+        red[(wave & 3) * 64 + lane] = s;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        float* dst = logits + (size_t)r * kExperts + e;
+        if (f32_nonfinite(*dst)) *dst = (float)(((red[lane] + red[64 + lane]) + red[128 + lane]) + red[192 + lane]);
+      }
+      __syncthreads();
+    }
+  }
+}
+
 template <bool Router, bool BT>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                          void* __restrict__ out, int rows, int mtiles) {
   using S = GemmShape<Router>;
   __shared__ __attribute__((aligned(1024))) char smem[kGStages * S::STAGE];
+  // router: rows of the tile with a non-finite logit (bit j of word b: row
+  // bm0 + 64 b + j)
+  __shared__ uint64_t bad_rows[Router ? kGBM / 64 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,6 +409,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   issue(0);
   issue(1);
   issue(2);
+  if (Router && tid < kGBM / 64) bad_rows[tid] = 0;
   vm_wait_stages<S::PER_WAVE>(full_wave, 2);
   __syncthreads();
   Ops o;
@@ -381,9 +462,17 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
       if constexpr (Router) {
         // expert group bn0 / 192, experts 32 wn + 16 j + m of its 64
         const int e0 = (bn0 / 192) * 64 + 32 * wn + m;
+        bool bad = false;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          static_cast<float*>(out)[(size_t)row * kExperts + e0 + 16 * j] = (float)sum64[i][j][t];
+        for (int j = 0; j < 2; ++j) {
+          const float v = (float)sum64[i][j][t];
+          static_cast<float*>(out)[(size_t)row * kExperts + e0 + 16 * j] = v;
+          bad |= f32_nonfinite(v);
+        }
+        if (bad) {
+          const int lr = row - bm0;
+          atomicOr((unsigned long long*)&bad_rows[lr >> 6], 1ull << (lr & 63));
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < S::NT; ++j) {
@@ -392,6 +481,16 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
         }
       }
     }
+  }
+  if constexpr (Router) {
+    __syncthreads();
+    uint64_t mask[kGBM / 64];
+    uint64_t any = 0;
+#pragma unroll
+    for (int b = 0; b < kGBM / 64; ++b) any |= (mask[b] = bad_rows[b]);
+    // (every stage's reads are done: the LDS stages are free)
+    if (any != 0)
+      router_recompute<BT>(x, w, static_cast<float*>(out), bm0, bn0 / 192, mask, reinterpret_cast<double*>(smem));
   }
 }
 
@@ -431,111 +530,6 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 #pragma unroll
   for (int q = 0; q < 3; ++q)
     *(u32x4*)(dst + 64 * q) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
-}
-
-// Router logits the GEMM returned as an infinity or a NaN, recomputed exactly.
-//
-// The GEMM multiplies the hidden row by three BF16 parts of each FP32 weight.
-// The parts can differ in sign or be zero, so an infinite hidden value gives
-// inf - inf or inf * 0 (NaN) where the single product x * w is an infinity;
-// and an FP32 chain can overflow where the full float64 dot stays finite. A
-// finite hidden row with no overflow never produces a non-finite logit, and
-// an infinite or NaN hidden value makes every logit of its row non-finite.
-// So every logit the GEMM returned non-finite is recomputed here as a plain
-// FP64 dot of the hidden row with the FP32 weight (rebuilt exactly as
-// hi + mid + lo from the packed parts, each sum exact in FP64), the four
-// K quarters added in a fixed order and rounded once to FP32; finite logits
-// are left as they are. One workgroup per 64 rows x 64 experts: a tile with
-// no non-finite logit (every tile of a finite chunk) only reads its 16 KB of
-// logits and returns.
-constexpr int kFixRows = 64;
-constexpr int kFixExperts = 64;
-
-__device__ __forceinline__ bool f32_nonfinite(float v) {
-  return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u;
-}
-
-template <bool Packed>
-__global__ __launch_bounds__(256) void router_fixup_kernel(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ wr,
-                                                           const uint16_t* __restrict__ parts_t,
-                                                           float* __restrict__ logits, int rows) {
-  __shared__ uint64_t bad_rows;      // bit j: row r0 + j has a non-finite logit in this tile
-  __shared__ double red[4][kFixExperts];
-  const int r0 = blockIdx.x * kFixRows;
-  const int e0 = blockIdx.y * kFixExperts;
-  const int t = threadIdx.x;
-  const int wave = t >> 6;
-  const int lane = t & 63;
-  // thread t checks row r0 + t / 4, experts e0 + 16 (t % 4) .. + 15
-  const int cr = r0 + (t >> 2);
-  bool bad = false;
-  if (cr < rows) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(logits + (size_t)cr * kExperts + e0 + 16 * (t & 3));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = p[q];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bad |= f32_nonfinite(v[c]);
-    }
-  }
-  if (t == 0) bad_rows = 0;
-  __syncthreads();
-  const uint64_t m = ballot(bad);    // lanes 4 j .. 4 j + 3 of wave w check row 16 w + j
-  if (lane == 0 && m != 0) {
-    uint64_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if ((m >> (4 * j)) & 15u) mine |= 1ull << (16 * wave + j);
-    atomicOr((unsigned long long*)&bad_rows, (unsigned long long)mine);
-  }
-  __syncthreads();
-  uint64_t todo = bad_rows;          // the same value in every thread
-  // thread (wave q, lane j): expert e0 + j over K quarter q
-  const int e = e0 + lane;
-  const int kb = wave * (kHidden / 4);
-  while (todo != 0) {
-    const int r = r0 + __builtin_ctzll(todo);
-    todo &= todo - 1;
-    const uint16_t* xr = x + (size_t)r * kHidden;
-    double s = 0.0;
-    if constexpr (Packed) {
-      // the parts of expert e: rows (e / 64) * 192 + 64 p + e % 64 of parts_t
-      const uint16_t* ph = parts_t + (size_t)((e / 64) * 192 + e % 64) * kHidden;
-      for (int k = kb; k < kb + kHidden / 4; k += 8) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + k);
-        const u32x4 hv = *reinterpret_cast<const u32x4*>(ph + k);
-        const u32x4 mv = *reinterpret_cast<const u32x4*>(ph + (size_t)64 * kHidden + k);
-        const u32x4 lv = *reinterpret_cast<const u32x4*>(ph + (size_t)128 * kHidden + k);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int h = i >> 1;
-          auto part = [&](uint32_t pair) { return (double)((i & 1) ? bf16_hi(pair) : bf16_lo(pair)); };
-          const double w = part(hv[h]) + part(mv[h]) + part(lv[h]);
-          s = fma(part(xv[h]), w, s);
-        }
-      }
-    } else {
-#pragma unroll 8
-      for (int k = kb; k < kb + kHidden / 4; ++k)
-        s = fma((double)__uint_as_float((uint32_t)xr[k] << 16), (double)wr[(size_t)k * kExperts + e], s);
-    }
-    red[wave][lane] = s;
-    __syncthreads();
-    if (wave == 0) {
-      float* dst = logits + (size_t)r * kExperts + e;
-      if (f32_nonfinite(*dst)) *dst = (float)(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
-    }
-    __syncthreads();
-  }
-}
-
-static hipError_t launch_router_fixup(const uint16_t* x, const float* wr, const uint16_t* parts_t,
-                                      float* logits, int rows, hipStream_t stream) {
-  const dim3 grid((rows + kFixRows - 1) / kFixRows, kExperts / kFixExperts);
-  return parts_t ? launch_kernel(router_fixup_kernel<true>, grid, dim3(256), stream, x, wr, parts_t, logits, rows)
-                 : launch_kernel(router_fixup_kernel<false>, grid, dim3(256), stream, x, wr, parts_t, logits,
-                                 rows);
 }
 
 // Packing for the K-contiguous GEMM variant, once per weight set, through
@@ -616,10 +610,8 @@ hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t
   hipError_t e = launch_kernel(prefill_gemm_kernel<false, true>, dim3(mt * (kLatent / 224)), dim3(kGThreads),
                                stream, x, wt, (void*)latent, rows, mt);
   if (e != hipSuccess) return e;
-  e = launch_kernel(prefill_gemm_kernel<true, true>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
-                    x, parts_t, (void*)logits, rows, mt);
-  if (e != hipSuccess) return e;
-  return launch_router_fixup(x, nullptr, parts_t, logits, rows, stream);
+  return launch_kernel(prefill_gemm_kernel<true, true>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
+                       x, parts_t, (void*)logits, rows, mt);
 }
 
 hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
@@ -629,10 +621,8 @@ hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint1
                                w_router, parts);
   if (e != hipSuccess) return e;
   const int mt = (rows + kGBM - 1) / kGBM;
-  e = launch_kernel(prefill_gemm_kernel<true, false>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
-                    x, (const uint16_t*)parts, (void*)logits, rows, mt);
-  if (e != hipSuccess) return e;
-  return launch_router_fixup(x, w_router, nullptr, logits, rows, stream);
+  return launch_kernel(prefill_gemm_kernel<true, false>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
+                       x, (const uint16_t*)parts, (void*)logits, rows, mt);
 }
 
 }  // namespace route
