@@ -194,7 +194,7 @@ def test_prefill_packed_layout():
     assert bool((mid[nz] <= hi[nz] * 2.0 ** -7).all())
 
 
-@pytest.mark.parametrize("rows", [1, 200, 3072])
+@pytest.mark.parametrize("rows", [1, 191, 193, 200, 2881, 3072])
 def test_prefill_packed_bitwise_equal_to_unpacked(rows):
     w, wr = weights_dev(0)
     plan, packed = prefill_packed(0)

@@ -68,8 +68,12 @@ def test_prefill_chunk_3072_outliers(bank):
     check_outputs(xs, got, f"prefill 3072 bank {bank}")
 
 
-@pytest.mark.parametrize("rows", [1, 77, 130, 1000])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rows", [1, 77, 130, 191, 192, 193, 384, 1000, 3071])
 def test_prefill_ragged(rows):
+    """Row counts around the 192-row block tile: one row, a partial first
+    tile, one row short of a tile, a whole tile, one row into the second,
+    two whole tiles, and one row short of the largest chunk."""
     log(f"prefill ragged rows={rows}")
     xs = gen.hidden(rows, bank=600 + rows, outliers=True)
     got = run_prefill(xs, cap=3072)
