@@ -269,3 +269,75 @@ def test_packed_graph_replay_mixed_widths_one_workspace():
     torch.cuda.synchronize()
     assert mismatches == 0
     assert decode_counters_idle(ws)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("packed", [False, True])
+def test_prefill_graph_replay(packed):
+    """The prefill route (both GEMMs and the top-16, 384 rows: two row tiles)
+    captured in one HIP graph with the outputs poisoned inside it. Replays
+    rotate over input banks, one of which holds infinite and NaN hidden
+    values (so the router GEMM's recompute of non-finite logits runs inside
+    the graph), with eager calls of the same plan and device synchronisations
+    between replays; every replay must equal the eager call on its bank."""
+    rows, nb, replays = 384, 6, 60
+    log(f"prefill graph replay packed={packed} rows={rows} replays={replays}")
+    w, wr = weights_dev(0)
+    plan = route.Plan(route.MODE_PREFILL, rows)
+    ws = plan.new_workspace()
+    pk = route.pack_weights(plan, w, wr) if packed else None
+    banks = []
+    for b in range(nb):
+        xs = gen.hidden(rows, bank=32000 + b, outliers=True)
+        if b == 2:
+            xs[5, 100] = 0x7F80    # +inf
+            xs[200, 7000] = 0xFF80  # -inf
+            xs[383, 0] = 0x7FC0    # NaN
+        banks.append(bf16_dev(xs))
+
+    def call(x, o):
+        if packed:
+            route.fused_packed(plan, x, pk, o.latent, o.logits, o.ids, o.weights, ws)
+        else:
+            route.fused(plan, x, w, wr, o.latent, o.logits, o.ids, o.weights, ws)
+
+    refs = []
+    for b in range(nb):
+        o = Outputs(rows)
+        call(banks[b], o)
+        refs.append(o)
+    torch.cuda.synchronize()
+
+    x_static = torch.empty_like(banks[0])
+    x_static.copy_(banks[0])
+    out = Outputs(rows)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out.poison()
+        call(x_static, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out.poison()
+        call(x_static, out)
+    torch.cuda.synchronize()
+
+    spare = Outputs(rows)
+    mismatches = 0
+    for i in range(replays):
+        b = (i * 5 + 2) % nb
+        x_static.copy_(banks[b])
+        g.replay()
+        torch.cuda.synchronize()
+        r = refs[b]
+        same = (torch.equal(out.latent.view(torch.int16), r.latent.view(torch.int16))
+                and torch.equal(out.logits.view(torch.int32), r.logits.view(torch.int32))
+                and torch.equal(out.ids, r.ids)
+                and torch.equal(out.weights.view(torch.int32), r.weights.view(torch.int32)))
+        mismatches += 0 if same else 1
+        # the program's own eager work between replays
+        call(banks[(b + 1) % nb], spare)
+        torch.cuda.synchronize()
+    assert mismatches == 0
