@@ -13,11 +13,12 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split (whole route with [K][N] weights; packed weights split K 8 ways
+// Work split (whole route with [K][N] weights up to 4 rows; above 4 rows the
+// [K][N] launch splits the router 8 ways, and packed weights split K 8 ways
 // for both weights up to 4 rows and 4 (latent) / 8 (router) ways above, see
-// PackedShape; a tensor-parallel rank's share uses the same units over its
-// columns with more K splits): 672 workgroups of 4 waves, all resident at
-// once.
+// KnWideShape and PackedShape; a tensor-parallel rank's share uses the same
+// units over its columns with more K splits): 672 workgroups of 4 waves, all
+// resident at once.
 //   workgroups 0..447, dispatched first: router units, expert tile (32
 //       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
 //       bytes) of the FP32 router weight and the unit stores one FP64 partial
@@ -111,13 +112,18 @@ using FullShape = DecodeShape<kLatent, kExperts, 4, 16>;
 //   4 x 8       18.0  18.0  18.0  18.5  19.2  19.7  21.0  21.2
 //   4 x 16      18.7    -     -   20.0  20.9  20.9    -   22.9
 // 8 x 8 gives every wave the same 28 KB to stream; 4 x 8 gives the latent
-// waves twice the router waves' bytes. With [K][N] weights 4 x 16 is faster
-// at every width.
+// waves twice the router waves' bytes. With [K][N] weights (each wave's loads
+// are 128-byte row segments) 4 x 16 is faster up to 4 rows and 4 x 8 with the
+// latent hold and router prefetch above (us per route, 1 / 8 / 12 / 16 / 20
+// rows, 4 x 16: 18.1 / 20.4-20.8 / 21.3 / 22.0 / 24.0; 4 x 8: 18.4 / 19.6-19.7
+// / 20.5-20.6 / 21.3-21.5 / 23.7-24.0; 4 x 8 without the hold 18.6 / 19.8 /
+// 20.6 / 21.3 / 24.6).
 using PackedShape = DecodeShape<kLatent, kExperts, 8, 8>;      // 1..4 rows
 using PackedWideShape = DecodeShape<kLatent, kExperts, 4, 8>;  // 5..20 rows
-constexpr int kPackedNarrowMaxRows = 4;
+using KnWideShape = DecodeShape<kLatent, kExperts, 4, 8>;      // [K][N] weights, 5..20 rows
+constexpr int kNarrowMaxRows = 4;
 
-// Latent units of a packed launch (8 router splits) hold their stream back
+// Latent units of a launch with 8 router splits hold their stream back
 // after they start, 2.6 us up to 16 rows and 3.6 us at 17..20 rows (ticks of
 // the 100 MHz realtime counter), so that the router's stream, which feeds the
 // longer chain of dependent steps (tile combine, router completion, top-16),
@@ -150,7 +156,8 @@ using Tp16Shape = DecodeShape<224, 56, 14, 28>;
 constexpr int kDecodeCounters = FullShape::Counters;   // the largest counter set
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters &&
-                  PackedShape::Counters == kDecodeCounters && PackedWideShape::Counters == kDecodeCounters,
+                  PackedShape::Counters == kDecodeCounters && PackedWideShape::Counters == kDecodeCounters &&
+                  KnWideShape::Counters == kDecodeCounters,
               "every shape's counters fit the workspace's counter area");
 static_assert(FullShape::LatTiles == 56 && FullShape::RtTiles == 28 && FullShape::Grid == 672, "full shape");
 
@@ -459,7 +466,7 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (Packed && latent_hold_ticks<NT, Sh>() > 0) {
+  if constexpr (latent_hold_ticks<NT, Sh>() > 0) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (__builtin_amdgcn_s_memrealtime() - t0 < latent_hold_ticks<NT, Sh>()) __builtin_amdgcn_s_sleep(2);
   }
@@ -697,8 +704,9 @@ size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off
   if (latent == Tp16Shape::N && experts == Tp16Shape::E)
     return ws_bytes<Tp16Shape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
   static_assert(PackedWideShape::SplitsL <= PackedShape::SplitsL &&
-                    PackedWideShape::SplitsR <= FullShape::SplitsR,
-                "the 4 x 8 packed launch fits the partial areas of the other two");
+                    PackedWideShape::SplitsR <= FullShape::SplitsR &&
+                    KnWideShape::SplitsL <= PackedShape::SplitsL && KnWideShape::SplitsR <= FullShape::SplitsR,
+                "the 4 x 8 launches fit the partial areas of the other two");
   return ws_bytes<FullShape, PackedShape>(rows_cap, off_lat, off_rt, off_logits, off_cand);
 }
 
@@ -731,9 +739,10 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, cons
   a.rows = rows;
   a.rows_cap = rows_cap;
   a.fuse_topk = fuse_topk ? 1 : 0;
-  if (full && packed && rows <= kPackedNarrowMaxRows) return launch_shape<PackedShape, true>(a, rows, stream);
+  if (full && packed && rows <= kNarrowMaxRows) return launch_shape<PackedShape, true>(a, rows, stream);
   if (full && packed) return launch_shape<PackedWideShape, true>(a, rows, stream);
-  if (full) return launch_shape<FullShape>(a, rows, stream);
+  if (full && rows <= kNarrowMaxRows) return launch_shape<FullShape>(a, rows, stream);
+  if (full) return launch_shape<KnWideShape>(a, rows, stream);
   if (n_latent == Tp8Shape::N) return launch_shape<Tp8Shape>(a, rows, stream);
   return launch_shape<Tp16Shape>(a, rows, stream);
 }
