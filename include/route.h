@@ -178,8 +178,11 @@ int route_topk16_sharded(const route_plan* plan, const float* logits, int32_t sh
  *     K order. The kernel splits K its own ways (8 for both weights up to 4
  *     rows, 4 for the latent and 8 for the router above); this K split
  *     differs from the [K][N] kernel's, so a latent value may differ from
- *     route_fused's in the last bit (each is one full-K dot rounded once).
- *     Logits are FP64 sums rounded once in both;
+ *     route_fused's in the last bit (each is one full-K dot rounded once),
+ *     and between a packed call of 1..4 rows and one of 5..20 rows. The
+ *     [K][N] kernel splits the latent 4 ways at every width, so its latent
+ *     for a row does not depend on the call's row count. Logits are FP64
+ *     sums rounded once in both;
  *   prefill: the weights K-contiguous, W as [3584][7168] BF16 (the [out][in]
  *     layout of a linear layer) and the router weight as its three exact
  *     BF16 parts [2688][7168] (split once here instead of on every call), so
