@@ -132,11 +132,16 @@ constexpr int kNarrowMaxRows = 4;
 // 17.2 / 18.1 / 19.0 us against 18.2 / 18.9 / 19.15 without it; holds of 2.0
 // and 3.2 us were slower than 2.6. 4 x 8 at 17 / 20 rows: 26.2 / 25.5 us
 // without a hold, 25.3 / 25.0 with 1.8 us, 22.7 / 22.6 with 2.6, 21.0 / 21.2
-// with 3.6 and 21.4 / 21.9 with 4.5. With 16 router splits (the router
-// stream already ends first) a hold did not help. A bounded wait on a clock,
-// not on another workgroup.
-template <int NT, class Sh>
-constexpr uint64_t latent_hold_ticks() { return Sh::SplitsR == 8 ? (NT == 1 ? 260 : 360) : 0; }
+// with 3.6 and 21.4 / 21.9 with 4.5. With [K][N] weights (4 x 8) 2.6 us is
+// also best up to 16 rows, and 17..20 rows take 4.2 us (17 / 20 rows
+// 23.0-23.2 / 23.2 us against 23.4 / 23.5-23.8 with 3.6 and 23.7-24.2 /
+// 23.8-24.1 with 3.0; 5.0 us 23.0-23.2 / 23.2-23.3). With 16
+// router splits (the router stream already ends first) a hold did not help.
+// A bounded wait on a clock, not on another workgroup.
+template <int NT, class Sh, bool Packed>
+constexpr uint64_t latent_hold_ticks() {
+  return Sh::SplitsR != 8 ? 0 : NT == 1 ? 260 : Packed ? 360 : 420;
+}
 
 // Router steps of loads kept in flight per wave. With 8 router splits a
 // router wave has 14 steps and, while the latent units hold, the memory to
@@ -466,9 +471,10 @@ __device__ bool latent_unit(const DecodeArgs& a, const int u, char* smem, int* s
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (latent_hold_ticks<NT, Sh>() > 0) {
+  if constexpr (latent_hold_ticks<NT, Sh, Packed>() > 0) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__builtin_amdgcn_s_memrealtime() - t0 < latent_hold_ticks<NT, Sh>()) __builtin_amdgcn_s_sleep(2);
+    while (__builtin_amdgcn_s_memrealtime() - t0 < latent_hold_ticks<NT, Sh, Packed>())
+      __builtin_amdgcn_s_sleep(2);
   }
   constexpr int kDepth = depth<NT>() < Sh::StepsL ? depth<NT>() : Sh::StepsL;
   u32x2 wv[kDepth][8];
