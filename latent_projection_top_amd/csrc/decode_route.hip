@@ -155,9 +155,13 @@ constexpr int router_depth() {
 }
 // Share splits measured on MI355X (graph-replayed launches over 616 MB of
 // distinct shares): with the tile combine's loads all in flight, fewer and
-// longer K chunks won over 28 latent / 56 router splits by 1.5 to 3 us.
+// longer K chunks won over 28 latent / 56 router splits by 1.5 to 3 us at 8
+// ranks (7 / 28: 7.4 / 8.3 / 11.5 us at 1 / 8 / 20 rows; 14 / 28, 14 / 14,
+// 7 / 14 and 28 / 28 were 0.4-1.9 us slower); the 16-rank share's four
+// latent tiles take 28 splits (28 / 28: 7.1 / 7.8 / 11.0 us against 7.4 /
+// 7.9 / 11.1 with 14 / 28).
 using Tp8Shape = DecodeShape<448, 112, 7, 28>;
-using Tp16Shape = DecodeShape<224, 56, 14, 28>;
+using Tp16Shape = DecodeShape<224, 56, 28, 28>;
 constexpr int kDecodeCounters = FullShape::Counters;   // the largest counter set
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 static_assert(Tp8Shape::Counters <= kDecodeCounters && Tp16Shape::Counters <= kDecodeCounters &&
