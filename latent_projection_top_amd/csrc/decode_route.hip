@@ -13,12 +13,14 @@
 // 9..20 decode rows through the pushed pair gather and standalone top-16",
 // voipmonitor/flare pull request 24, "What / why").
 //
-// Work split (whole route with [K][N] weights up to 4 rows; above 4 rows the
-// [K][N] launch splits the router 8 ways, and packed weights split K 8 ways
-// for both weights up to 4 rows and 4 (latent) / 8 (router) ways above, see
-// KnWideShape and PackedShape; a tensor-parallel rank's share uses the same
-// units over its columns with more K splits): 672 workgroups of 4 waves, all
-// resident at once.
+// Work split, described for [K][N] weights at 1..4 rows (4 latent x 16
+// router K splits). Above 4 rows the [K][N] launch splits the router 8 ways
+// (KnWideShape, 448 workgroups); packed weights split K 8 ways for both
+// weights up to 4 rows and 4 (latent) / 8 (router) ways above (PackedShape,
+// PackedWideShape); the 8-way router launches hold their latent stream back
+// (latent_hold_ticks). A tensor-parallel rank's share uses the same units
+// over its columns with more K splits. Every launch's workgroups are
+// resident at once; here 672 workgroups of 4 waves:
 //   workgroups 0..447, dispatched first: router units, expert tile (32
 //       experts) x K chunk of 448 rows; each wave streams 112 rows (14,336
 //       bytes) of the FP32 router weight and the unit stores one FP64 partial
@@ -26,10 +28,11 @@
 //   workgroups 448..671: latent units, column tile (64 columns) x K chunk of
 //       1792 rows; each wave streams 448 rows (57,344 bytes) of the BF16 latent
 //       weight; the last unit of a tile sums the 4 partials and rounds once.
-// Router waves have a quarter of a latent wave's bytes and finish early; the
-// workgroup that combines the last router tile then selects the top-16 of
-// every row, four rows at a time (one per wave), while the latent weight is
-// still streaming, and latent workgroups take any rows left when they finish.
+// Router waves have a quarter of a latent wave's bytes (half with 8 router
+// splits) and finish first; the workgroup that combines the last router tile
+// then selects the top-16 of every row, four rows at a time (one per wave),
+// while the latent weight is still streaming, and latent workgroups take any
+// rows left when they finish.
 // Nothing ever waits for another workgroup; every unit's arithmetic and
 // combine order is fixed, so results do not depend on scheduling.
 //
