@@ -511,6 +511,9 @@ def main():
             lambda: [route.latent_router_packed(plan, x, packed, lat, lg, ws) for _ in range(10)], torch)
         t_all_kn = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr_kn = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
+        # the pages' other chunk size: 1024 rows (6 row tiles, K split in 2)
+        t_1024 = t_call(lambda: route.fused_packed(plan, x[:1024], packed, lat[:1024], lg[:1024], ids[:1024],
+                                                   wt[:1024], ws, rows=1024), args.prefill_reps)
         del packed, p
         method_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER
         mfma_flops = PREFILL_FLOPS_LATENT + PREFILL_FLOPS_ROUTER_MFMA
@@ -533,6 +536,10 @@ def main():
                            "rows_per_s": round(rows / (t_all_kn * 1e-6)),
                            "latent_router_us": round(t_lr_kn, 2),
                            "note": "[K][N] weights; includes the per-call router weight split"},
+            "chunk_1024": {"rows": 1024, "us_per_chunk": round(t_1024, 2),
+                           "rows_per_s": round(1024 / (t_1024 * 1e-6)),
+                           "note": "packed weights, the same plan; chunks of 1..1728 rows split K over more "
+                                   "workgroups (1024 rows: 2 splits)"},
         }
         log(f"prefill 3072 (packed): {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
             f"{t_lr:.1f} us = {prefill['method_tflops']} TFLOP/s of the method's work "

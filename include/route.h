@@ -134,7 +134,10 @@ size_t route_workspace_bytes(const route_plan* plan);
  * parts of each FP32 weight, then recompute every logit that came out as an
  * infinity or a NaN (a hidden row holding an infinity or a NaN, or an FP32
  * partial sum that overflowed) as an exact FP64 dot, so such rows get the
- * plain dot's IEEE result. */
+ * plain dot's IEEE result. Prefill calls of at most 1,728 rows split K over
+ * more workgroups (their partial sums go through the workspace and are added
+ * in FP64 before the single rounding), so a row's last bit may depend on the
+ * call's row count; calls of more rows do not split. */
 int route_latent_router(const route_plan* plan, const void* x, const void* w_latent,
                         const float* w_router, void* latent, float* logits,
                         void* workspace, int32_t rows, void* stream);
@@ -227,7 +230,11 @@ int route_fused_packed(const route_plan* plan, const void* x, const void* packed
  * plans use it only for the logits when `logits` is NULL, at most
  * ROUTE_STATIC_SCRATCH_BYTES - 512 bytes (rows * 3584 bytes), and return
  * ROUTE_E_SCRATCH above that. Outputs are bitwise those of route_fused_packed
- * on the same plan. Every call on a GPU shares that GPU's array, and the
+ * on the same plan, except prefill calls of at most 1,728 rows: there
+ * route_fused_packed splits K with partials in its workspace and this call
+ * does not (the static scratch cannot hold them), so a value may differ in
+ * the last bit, both within the same bounds. Every call on a GPU shares that
+ * GPU's array, and the
  * decode counters carry over from call to call: two calls that overlap in
  * time on one GPU (different streams, threads or graphs running at once)
  * race on it and must not be issued. Other statuses as route_fused_packed;

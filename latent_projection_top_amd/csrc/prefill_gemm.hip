@@ -69,6 +69,7 @@ constexpr int kRouterCols = 3 * kExperts;  // 2688: [14 groups][3 parts][64]
 static_assert(kGKT % kGFoldStages == 0, "fold period");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool Router>
@@ -146,7 +147,8 @@ __device__ __forceinline__ bool f32_nonfinite(float v) {
 }
 
 // Router logits the GEMM returned as an infinity or a NaN, recomputed exactly
-// by the workgroup that computed them.
+// by the workgroup that computed them (or, for a K-split launch, that
+// combined them).
 //
 // The GEMM multiplies the hidden row by three BF16 parts of each FP32 weight.
 // The parts can differ in sign or be zero, so an infinite hidden value gives
@@ -221,7 +223,7 @@ __device__ void router_recompute(const uint16_t* __restrict__ x, const uint16_t*
 template <bool Router, bool BT>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                         void* __restrict__ out, int rows, int mtiles) {
+                         void* __restrict__ out, int rows, int mtiles, int nsplit, void* __restrict__ part) {
   using S = GemmShape<Router>;
   __shared__ __attribute__((aligned(1024))) char smem[kGStages * S::STAGE];
   // router: rows of the tile with a non-finite logit (bit j of word b: row
@@ -241,10 +243,18 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   // divides evenly), giving each XCD a contiguous range; the range is then
   // walked in groups of 8 row tiles, column by column, so that one XCD's L2
   // holds about 8 A tiles and 4 B tiles at a time.
+  // With nsplit > 1 (few row tiles) the blocks of K split q are the q-th run
+  // of `total` blocks, each over K stages [q nkt, (q + 1) nkt), and write
+  // their FP32 (latent) or FP64 (router) sums to `part` for a combine pass.
   const int ntiles = S::N / S::BN;
   const int total = mtiles * ntiles;
-  int lin = blockIdx.x;
-  if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int split = blockIdx.x / total;
+  const int bid = blockIdx.x - split * total;
+  const int nkt = kGKT / nsplit;
+  const int kt0 = split * nkt;
+  const int kend = kt0 + nkt;
+  int lin = bid;
+  if ((total & 7) == 0) lin = (bid & 7) * (total >> 3) + (bid >> 3);
   const int grp = lin / (8 * ntiles);
   const int first = grp * 8;
   const int gm = min(mtiles - first, 8);
@@ -406,26 +416,26 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   // meets the others at the barrier: past it, stage kt + 1 is complete in
   // LDS and stage kt's buffer takes the loads of stage kt + 3, while the
   // second half runs and reads the first half of stage kt + 1.
-  issue(0);
-  issue(1);
-  issue(2);
+  issue(kt0);
+  issue(kt0 + 1);
+  issue(kt0 + 2);
   if (Router && tid < kGBM / 64) bad_rows[tid] = 0;
   vm_wait_stages<S::PER_WAVE>(full_wave, 2);
   __syncthreads();
   Ops o;
 #pragma unroll
-  for (int i = 0; i < S::MT; ++i) o.a[i] = read_a(stage_lds(0), 0, i);
+  for (int i = 0; i < S::MT; ++i) o.a[i] = read_a(stage_lds(kt0), 0, i);
 #pragma unroll
-  for (int j = 0; j < S::NT; ++j) o.b[j] = read_b(stage_lds(0), 0, j);
+  for (int j = 0; j < S::NT; ++j) o.b[j] = read_b(stage_lds(kt0), 0, j);
 
 #pragma unroll 1
-  for (int kp = 0; kp < kGKT; kp += kGFoldStages) {
+  for (int kp = kt0; kp < kend; kp += kGFoldStages) {
 #pragma unroll
     for (int u = 0; u < kGFoldStages; ++u) {
       const int kt = kp + u;
       step(o, u == 0, true, stage_lds(kt), 1, -1);
       lgkm_wait0();
-      vm_wait_stages<S::PER_WAVE>(full_wave, kt + 2 < kGKT ? 1 : 0);
+      vm_wait_stages<S::PER_WAVE>(full_wave, kt + 2 < kend ? 1 : 0);
       __syncthreads();
       // (after the last stage this reads a stale buffer; the values go unused)
       // Stage kt + 3's loads: the router GEMM spreads them over the second
@@ -433,8 +443,8 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
       // barrier (measured: latent + router 239.9 against 245.8 us, 4
       // interleaved pairs); the latent GEMM issues them together, because
       // spreading them there spills 42 registers.
-      if (!Router && kt + 3 < kGKT) issue(kt + 3);
-      step(o, false, true, stage_lds(kt + 1), 0, Router && kt + 3 < kGKT ? kt + 3 : -1);
+      if (!Router && kt + 3 < kend) issue(kt + 3);
+      step(o, false, true, stage_lds(kt + 1), 0, Router && kt + 3 < kend ? kt + 3 : -1);
     }
     // fold the restarted chains into the long sums
 #pragma unroll
@@ -453,6 +463,29 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   }
 
   // lane (g, m) of tile (i, j) holds row 16 i + 4 g + t, column 16 j + m
+  if (part != nullptr) {
+    // split partials [nsplit][rows][N]: latent FP32, router FP64
+#pragma unroll
+    for (int i = 0; i < S::MT; ++i) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = bm0 + 48 * wm + 16 * i + 4 * g + t;
+        if (row >= rows) continue;
+        if constexpr (Router) {
+          const int e0 = (bn0 / 192) * 64 + 32 * wn + m;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            static_cast<double*>(part)[((size_t)split * rows + row) * kExperts + e0 + 16 * j] = sum64[i][j][t];
+        } else {
+#pragma unroll
+          for (int j = 0; j < S::NT; ++j)
+            static_cast<float*>(part)[((size_t)split * rows + row) * kLatent + bn0 + tile_col<false>(wn, j) + m] =
+                sum32[i][j][t];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < S::MT; ++i) {
 #pragma unroll
@@ -492,6 +525,107 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     if (any != 0)
       router_recompute<BT>(x, w, static_cast<float*>(out), bm0, bn0 / 192, mask, reinterpret_cast<double*>(smem));
   }
+}
+
+// K splits for chunks of few row tiles. A GEMM block streams its whole
+// weight tile (224 or 192 columns x 7168 K) through one CU, so with few row
+// tiles the GEMMs use a fraction of the 256 CUs and take about as long as a
+// full 3072-row chunk (measured 203-215 us per packed chunk for 64 to 2048
+// rows unsplit). Splitting K fills the chip; the cost is the partials' round
+// trip through HBM and a combine pass. The split of each GEMM by row tiles
+// comes from a model of one block's full-K time and the partials' traffic,
+// over splits whose K stages are whole fold periods (112 / S a multiple of
+// 4), checked by measurement: packed chunks of 64 / 192 / 384 / 768 / 1024 /
+// 1536 / 1728 rows take 40 / 52 / 64 / 88 / 129 / 144 / 187 us against 204 /
+// 209 / 209 / 211 / 211 / 214 / 214 unsplit (A/B, one box; 2048 and 3072
+// rows are not split and unchanged). Every output is still one sum over all
+// of K rounded once: the combine adds the splits' FP32 (latent) or FP64
+// (router) sums in split order in FP64. The split changes the order of the
+// FP32 additions, so a row's last bit may depend on the chunk's row count.
+int prefill_splits(int mtiles, bool router) {
+  if (mtiles <= 1) return 14;
+  if (mtiles == 2) return 7;
+  if (mtiles <= 4) return 4;
+  if (mtiles <= 8 || (router && mtiles == 9)) return 2;
+  return 1;
+}
+
+// Latent combine: latent[r][n] = BF16(sum over splits of part[q][r][n]), the
+// sum in FP64 in split order, one rounding. 4 outputs per thread; the split
+// count is a template argument so that every split's load is in flight
+// before the first add.
+template <int NS>
+__global__ __launch_bounds__(256) void latent_combine_kernel(const float* __restrict__ part,
+                                                             uint16_t* __restrict__ latent, int rows) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * (kLatent / 4)) return;
+  const size_t plane = (size_t)rows * kLatent;
+  f32x4 v[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) v[q] = *reinterpret_cast<const f32x4*>(part + q * plane + 4 * i);
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int q = 0; q < NS; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += (double)v[q][c];
+  u32x2 o;
+  o[0] = (uint32_t)f64_to_bf16_rne(acc[0]) | ((uint32_t)f64_to_bf16_rne(acc[1]) << 16);
+  o[1] = (uint32_t)f64_to_bf16_rne(acc[2]) | ((uint32_t)f64_to_bf16_rne(acc[3]) << 16);
+  *reinterpret_cast<u32x2*>(latent + 4 * i) = o;
+}
+
+// Router combine: logits[r][e] = FP32(sum over splits of part[q][r][e]) in
+// FP64 split order, then the exact recompute of any non-finite logit. One
+// workgroup per 16 rows x 64 experts (enough workgroups to spread the
+// partials' loads at one row tile); thread t sums row r0 + t / 16, experts
+// e0 + 4 (t % 16) .. + 3.
+constexpr int kCombRows = 16;
+
+template <bool BT, int NS>
+__global__ __launch_bounds__(256) void router_combine_kernel(const double* __restrict__ part,
+                                                             float* __restrict__ logits, int rows,
+                                                             const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ parts_w) {
+  __shared__ uint64_t bad_rows;
+  __shared__ double red[256];
+  const int r0 = blockIdx.x * kCombRows;
+  const int e0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int r = r0 + (t >> 4);
+  bool bad = false;
+  if (r < rows) {
+    const size_t plane = (size_t)rows * kExperts;
+    const double* src = part + (size_t)r * kExperts + e0 + 4 * (t & 15);
+    f64x2 v[NS][2];
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) v[q][h] = *reinterpret_cast<const f64x2*>(src + q * plane + 2 * h);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += v[q][c >> 1][c & 1];
+    const f32x4 o = {(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]};
+    *reinterpret_cast<f32x4*>(logits + (size_t)r * kExperts + e0 + 4 * (t & 15)) = o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bad |= f32_nonfinite(o[c]);
+  }
+  if (t == 0) bad_rows = 0;
+  __syncthreads();
+  const uint64_t m = ballot(bad);    // lanes 16 j .. 16 j + 15 of wave w hold row 4 w + j
+  if (lane == 0 && m != 0) {
+    uint64_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((m >> (16 * j)) & 0xFFFFu) mine |= 1ull << (4 * wave + j);
+    atomicOr((unsigned long long*)&bad_rows, (unsigned long long)mine);
+  }
+  __syncthreads();
+  const uint64_t mask[kGBM / 64] = {bad_rows, 0ull, 0ull};
+  if (mask[0] != 0) router_recompute<BT>(x, parts_w, logits, r0, e0 / 64, mask, red);
 }
 
 // The three exact BF16 parts of an FP32 weight: each takes the top 8
@@ -583,46 +717,100 @@ hipError_t launch_pack_prefill_weights(const uint16_t* w_latent, const float* w_
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand) {
+// Bytes of the K-split partials of a call of `rows` rows: the latent GEMM's
+// FP32 and the router GEMM's FP64 sums per split, one after the other in
+// time, so they share one area.
+static size_t split_part_bytes(int rows) {
+  const int mt = (rows + kGBM - 1) / kGBM;
+  const int sl = prefill_splits(mt, false);
+  const int sr = prefill_splits(mt, true);
+  const size_t lat = sl > 1 ? (size_t)sl * rows * kLatent * sizeof(float) : 0;
+  const size_t rt = sr > 1 ? (size_t)sr * rows * kExperts * sizeof(double) : 0;
+  return lat > rt ? lat : rt;
+}
+
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand,
+                               size_t* off_split) {
   *off_parts = 0;
   size_t off = align256(sizeof(uint16_t) * (size_t)kHidden * kRouterCols);
   *off_logits = off;
   off += align256(sizeof(float) * (size_t)rows_cap * kExperts);
   *off_cand = off;
-  return off + align256(sizeof(uint64_t) * (size_t)rows_cap * kTopkMaxShards * kTopK);
+  off += align256(sizeof(uint64_t) * (size_t)rows_cap * kTopkMaxShards * kTopK);
+  *off_split = off;
+  // the largest split area over every row count the plan accepts (it peaks
+  // at the last row of some row tile)
+  size_t most = 0;
+  for (int mt = 1; mt * kGBM - kGBM < rows_cap; ++mt) {
+    const size_t b = split_part_bytes(mt * kGBM < rows_cap ? mt * kGBM : rows_cap);
+    most = b > most ? b : most;
+  }
+  return off + align256(most);
 }
 
-hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
-                                 int rows, hipStream_t stream) {
-  if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
+// One GEMM over `rows` rows, K-split when `part` is given and the row tiles
+// are few, then the combine of the split sums.
+template <bool Router, bool BT>
+static hipError_t launch_gemm(const uint16_t* x, const uint16_t* w, void* out, int rows, void* part,
+                              hipStream_t stream) {
+  using S = GemmShape<Router>;
   const int mt = (rows + kGBM - 1) / kGBM;
-  return launch_kernel(prefill_gemm_kernel<false, false>, dim3(mt * (kLatent / 224)), dim3(kGThreads), stream,
-                       x, w_latent, (void*)latent, rows, mt);
+  const int ns = part != nullptr ? prefill_splits(mt, Router) : 1;
+  const int blocks = mt * (S::N / S::BN) * ns;
+  hipError_t e = launch_kernel(prefill_gemm_kernel<Router, BT>, dim3(blocks), dim3(kGThreads), stream, x, w, out,
+                               rows, mt, ns, ns > 1 ? part : nullptr);
+  if (e != hipSuccess || ns == 1) return e;
+  if constexpr (Router) {
+    const dim3 grid((rows + kCombRows - 1) / kCombRows, kExperts / 64);
+    const double* pp = static_cast<const double*>(part);
+    float* lg = static_cast<float*>(out);
+    switch (ns) {
+      case 2: return launch_kernel(router_combine_kernel<BT, 2>, grid, dim3(256), stream, pp, lg, rows, x, w);
+      case 4: return launch_kernel(router_combine_kernel<BT, 4>, grid, dim3(256), stream, pp, lg, rows, x, w);
+      case 7: return launch_kernel(router_combine_kernel<BT, 7>, grid, dim3(256), stream, pp, lg, rows, x, w);
+      case 14: return launch_kernel(router_combine_kernel<BT, 14>, grid, dim3(256), stream, pp, lg, rows, x, w);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    const dim3 grid((unsigned)(((size_t)rows * (kLatent / 4) + 255) / 256));
+    const float* pp = static_cast<const float*>(part);
+    uint16_t* lt = static_cast<uint16_t*>(out);
+    switch (ns) {
+      case 2: return launch_kernel(latent_combine_kernel<2>, grid, dim3(256), stream, pp, lt, rows);
+      case 4: return launch_kernel(latent_combine_kernel<4>, grid, dim3(256), stream, pp, lt, rows);
+      case 7: return launch_kernel(latent_combine_kernel<7>, grid, dim3(256), stream, pp, lt, rows);
+      case 14: return launch_kernel(latent_combine_kernel<14>, grid, dim3(256), stream, pp, lt, rows);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+static_assert(kGKT % (28 * kGFoldStages) == 0, "every split of the K stages is whole fold periods");
+
+hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
+                                 int rows, void* part, hipStream_t stream) {
+  if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
+  return launch_gemm<false, false>(x, w_latent, latent, rows, part, stream);
 }
 
 hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t* latent, float* logits,
-                                 int rows, hipStream_t stream) {
+                                 int rows, void* part, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
   const uint16_t* wt = static_cast<const uint16_t*>(packed);
   const uint16_t* parts_t =
       reinterpret_cast<const uint16_t*>(static_cast<const char*>(packed) + prefill_packed_latent_bytes());
-  const int mt = (rows + kGBM - 1) / kGBM;
-  hipError_t e = launch_kernel(prefill_gemm_kernel<false, true>, dim3(mt * (kLatent / 224)), dim3(kGThreads),
-                               stream, x, wt, (void*)latent, rows, mt);
+  const hipError_t e = launch_gemm<false, true>(x, wt, latent, rows, part, stream);
   if (e != hipSuccess) return e;
-  return launch_kernel(prefill_gemm_kernel<true, true>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
-                       x, parts_t, (void*)logits, rows, mt);
+  return launch_gemm<true, true>(x, parts_t, logits, rows, part, stream);
 }
 
 hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
-                                 float* logits, int rows, hipStream_t stream) {
+                                 float* logits, int rows, void* part, hipStream_t stream) {
   if (rows < 1 || rows > kPrefillMaxRows) return hipErrorInvalidValue;
-  hipError_t e = launch_kernel(router_split_kernel, dim3(kHidden * (kExperts / 8) / 256), dim3(256), stream,
-                               w_router, parts);
+  const hipError_t e = launch_kernel(router_split_kernel, dim3(kHidden * (kExperts / 8) / 256), dim3(256),
+                                     stream, w_router, parts);
   if (e != hipSuccess) return e;
-  const int mt = (rows + kGBM - 1) / kGBM;
-  return launch_kernel(prefill_gemm_kernel<true, false>, dim3(mt * (kRouterCols / 192)), dim3(kGThreads), stream,
-                       x, (const uint16_t*)parts, (void*)logits, rows, mt);
+  return launch_gemm<true, false>(x, parts, logits, rows, part, stream);
 }
 
 }  // namespace route

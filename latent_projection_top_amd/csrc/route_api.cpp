@@ -22,6 +22,7 @@ struct route_plan {
   size_t off_logits;  // logits buffer for route_fused with logits == NULL
   size_t off_parts;   // prefill: BF16 parts of the router weight
   size_t off_cand;    // sharded top-16 candidates
+  size_t off_split;   // prefill: K-split partials of chunks with few row tiles
 };
 
 namespace {
@@ -54,9 +55,9 @@ route::DecodeWorkspace decode_ws(const route_plan* p, void* ws) {
 }
 
 int run_prefill_packed(const void* x, const void* packed, void* latent, float* logits, int32_t* ids,
-                       float* weights, int32_t rows, bool fused, hipStream_t s) {
+                       float* weights, int32_t rows, bool fused, void* split, hipStream_t s) {
   int st = status_of(route::launch_prefill_packed(static_cast<const uint16_t*>(x), packed,
-                                                  static_cast<uint16_t*>(latent), logits, rows, s));
+                                                  static_cast<uint16_t*>(latent), logits, rows, split, s));
   if (st != ROUTE_OK || !fused) return st;
   return status_of(route::launch_topk16(logits, ids, weights, rows, s));
 }
@@ -66,7 +67,8 @@ int run_latent_router(const route_plan* p, const void* x, const void* w_latent, 
                       int32_t rows, bool fused, hipStream_t s, bool packed = false) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   if (packed && p->mode == ROUTE_MODE_PREFILL)
-    return run_prefill_packed(x, w_latent, latent, logits, ids, weights, rows, fused, s);
+    return run_prefill_packed(x, w_latent, latent, logits, ids, weights, rows, fused,
+                              static_cast<char*>(ws) + p->off_split, s);
   const uint16_t* wb = static_cast<const uint16_t*>(w_latent);
   uint16_t* lb = static_cast<uint16_t*>(latent);
   if (p->mode == ROUTE_MODE_DECODE) {
@@ -75,10 +77,11 @@ int run_latent_router(const route_plan* p, const void* x, const void* w_latent, 
                                                 decode_ws(p, ws), rows, p->rows_cap, p->latent,
                                                 p->experts, fused, packed, s));
   }
-  int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, s));
+  void* split = static_cast<char*>(ws) + p->off_split;
+  int st = status_of(route::launch_prefill_latent(xb, wb, lb, rows, split, s));
   if (st != ROUTE_OK) return st;
   uint16_t* parts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p->off_parts);
-  st = status_of(route::launch_prefill_router(xb, w_router, parts, logits, rows, s));
+  st = status_of(route::launch_prefill_router(xb, w_router, parts, logits, rows, split, s));
   if (st != ROUTE_OK || !fused) return st;
   return status_of(route::launch_topk16(logits, ids, weights, rows, s));
 }
@@ -139,10 +142,11 @@ int route_prepare(const route_config* cfg, route_plan** out) {
   if (p->mode == ROUTE_MODE_DECODE) {
     p->ws_bytes = route::decode_workspace_bytes(p->rows_cap, p->latent, p->experts, &p->off_lat,
                                                 &p->off_rt, &p->off_logits, &p->off_cand);
-    p->off_parts = 0;
+    p->off_parts = p->off_split = 0;
   } else {
     p->off_lat = p->off_rt = 0;
-    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits, &p->off_parts, &p->off_cand);
+    p->ws_bytes = route::prefill_workspace_bytes(p->rows_cap, &p->off_logits, &p->off_parts, &p->off_cand,
+                                                 &p->off_split);
   }
   *out = p;
   return ROUTE_OK;
@@ -280,7 +284,8 @@ int route_fused_packed_noalloc(const route_plan* plan, const void* x, const void
     if ((size_t)rows * ROUTE_EXPERTS * sizeof(float) > cap - off) return ROUTE_E_SCRATCH;
     lg = reinterpret_cast<float*>(static_cast<char*>(scratch) + off);
   }
-  return run_prefill_packed(x, packed, latent, lg, ids, weights, rows, true, s);
+  // (no workspace for K-split partials: the GEMMs run unsplit)
+  return run_prefill_packed(x, packed, latent, lg, ids, weights, rows, true, nullptr, s);
 }
 
 void route_destroy(route_plan* plan) { delete plan; }

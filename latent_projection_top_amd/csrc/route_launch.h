@@ -40,7 +40,8 @@ struct DecodeWorkspace {
 bool decode_shape_valid(int latent, int experts);
 size_t decode_workspace_bytes(int rows_cap, int latent, int experts, size_t* off_lat, size_t* off_rt,
                               size_t* off_logits, size_t* off_cand);
-size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand);
+size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_parts, size_t* off_cand,
+                               size_t* off_split);
 
 hipError_t launch_decode_route(const uint16_t* x, const uint16_t* w_latent, const float* w_router,
                                uint16_t* latent, float* logits, int32_t* ids, float* weights,
@@ -78,12 +79,14 @@ bool topk16_shards_valid(int shards);
 hipError_t launch_topk16_sharded(const float* logits, int shards, int32_t* ids, float* weights,
                                  uint64_t* cand, int rows, hipStream_t stream);
 
+// `part`: the workspace's K-split area, or NULL for launches that may not
+// split (the allocation-free entry point).
 hipError_t launch_prefill_latent(const uint16_t* x, const uint16_t* w_latent, uint16_t* latent,
-                                 int rows, hipStream_t stream);
+                                 int rows, void* part, hipStream_t stream);
 
 // parts: workspace for the three BF16 parts of w_router ([7168][2688] BF16)
 hipError_t launch_prefill_router(const uint16_t* x, const float* w_router, uint16_t* parts,
-                                 float* logits, int rows, hipStream_t stream);
+                                 float* logits, int rows, void* part, hipStream_t stream);
 
 // Packed prefill weights: W as [3584][7168] BF16, then the router weight's
 // three exact BF16 parts as [2688][7168] (K contiguous); the GEMMs read them
@@ -93,6 +96,6 @@ size_t prefill_packed_bytes();
 hipError_t launch_pack_prefill_weights(const uint16_t* w_latent, const float* w_router, void* packed,
                                        hipStream_t stream);
 hipError_t launch_prefill_packed(const uint16_t* x, const void* packed, uint16_t* latent, float* logits,
-                                 int rows, hipStream_t stream);
+                                 int rows, void* part, hipStream_t stream);
 
 }  // namespace route

@@ -69,11 +69,13 @@ def test_prefill_chunk_3072_outliers(bank):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("rows", [1, 77, 130, 191, 192, 193, 384, 1000, 3071])
+@pytest.mark.parametrize("rows", [1, 77, 130, 191, 192, 193, 384, 700, 1000, 1700, 3071])
 def test_prefill_ragged(rows):
-    """Row counts around the 192-row block tile: one row, a partial first
-    tile, one row short of a tile, a whole tile, one row into the second,
-    two whole tiles, and one row short of the largest chunk."""
+    """Row counts around the 192-row block tile and across the K splits of
+    chunks with few row tiles: one row, a partial first tile, one row short
+    of a tile, a whole tile (14 splits), one row into the second tile and two
+    whole tiles (7), four tiles (4), six tiles (2), nine tiles (the router
+    alone split in 2), and one row short of the largest chunk (unsplit)."""
     log(f"prefill ragged rows={rows}")
     xs = gen.hidden(rows, bank=600 + rows, outliers=True)
     got = run_prefill(xs, cap=3072)

@@ -1,7 +1,11 @@
 """The allocation-free entry point (route_fused_packed_noalloc) against the
-entry point it varies (route_fused_packed with a caller workspace): bitwise
-the same outputs on two calls in a row, the second with fewer rows, for
-decode and prefill plans, and both against the oracle. Nothing here
+entry point it varies (route_fused_packed with a caller workspace), on calls
+in a row, each with fewer rows than the one before, for decode and prefill
+plans, and both against the oracle: bitwise the same outputs wherever both
+run the same launches (every decode call; prefill calls of more than 1,728
+rows). Prefill calls of fewer rows split K in route_fused_packed, whose
+workspace holds the split partials, and not in the allocation-free call, so
+there the two are compared through the oracle's bounds. Nothing here
 allocates between the calls but the test's own output tensors."""
 import numpy as np
 import pytest
@@ -67,12 +71,18 @@ def test_noalloc_prefill_two_calls_and_capacity():
     plan = route.Plan(route.MODE_PREFILL, 3072)
     ws = plan.new_workspace()
     packed = route.pack_weights(plan, w, wr)
-    for rows, bank, with_logits in ((200, 8200, False), (77, 8201, False), (300, 8202, True)):
+    for rows, bank, with_logits in ((3072, 8203, True), (2112, 8204, True), (300, 8202, True),
+                                    (200, 8200, False), (77, 8201, False)):
         log(f"noalloc prefill rows={rows} logits={'given' if with_logits else 'scratch'}")
         xs = gen.hidden(rows, bank=bank, outliers=True)
         r, g = run_pair(plan, bf16_dev(xs), packed, rows, ws, with_logits)
-        assert_bitwise(r, g, with_logits)
-        check_oracle(xs, g, decode=False)
+        if rows > 1728:
+            assert_bitwise(r, g, with_logits)
+            if rows <= 2112:
+                check_oracle(xs, g, decode=False)
+        else:
+            check_oracle(xs, g, decode=False)
+            check_oracle(xs, r, decode=False)
     # the static scratch holds the logits of at most this many rows; one more
     # is rejected before anything is launched
     fit = (route.STATIC_SCRATCH_BYTES - 512) // (route.EXPERTS * 4)
