@@ -107,12 +107,17 @@ def test_decode_nonfinite_rows(packed):
         check_good_rows(got, ref, good, logits_ulp=True)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("rows", [96, 700, 2112])
 @pytest.mark.parametrize("packed", [False, True])
-def test_prefill_nonfinite_rows(packed):
-    log(f"prefill with inf / NaN hidden values, packed={packed}")
+def test_prefill_nonfinite_rows(packed, rows):
+    """Both weight layouts, on a chunk whose GEMMs split K in 14 (96 rows) or
+    4 (700 rows), where the router's combine pass recomputes the non-finite
+    logits, and on one that does not split (2112 rows), where the router
+    GEMM's own epilogue does."""
+    log(f"prefill with inf / NaN hidden values, packed={packed}, rows={rows}")
     w, wr = weights_dev(0)
-    rows = 96
-    xs, bad = poisoned_rows(rows, bank=700)
+    xs, bad = poisoned_rows(rows, bank=700 + rows)
     plan = route.Plan(route.MODE_PREFILL, rows)
     ws = plan.new_workspace()
     o = Outputs(rows)
