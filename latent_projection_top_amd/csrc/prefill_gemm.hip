@@ -26,7 +26,8 @@
 //
 // Tiling for gfx950 (256 CUs): block tile 192 rows x 224 columns (latent) or
 // 192 x 192 (router: 64 experts x 3 parts), so 3072 rows give 256 latent
-// blocks, one per CU. Eight waves, 4 x 2, each 48 rows x (112 | 96) columns
+// blocks, one per CU; chunks of few row tiles also split K over more blocks
+// (prefill_splits). Eight waves, 4 x 2, each 48 rows x (112 | 96) columns
 // with its accumulators in VGPRs: two waves per SIMD keep the matrix core
 // busy where one wave holding everything in AGPRs reaches only about 55% of
 // its rate. K step 64, three LDS stages (156 KB at most). Operands go from global
