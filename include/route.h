@@ -233,7 +233,8 @@ int route_fused_packed(const route_plan* plan, const void* x, const void* packed
  * on the same plan, except prefill calls of at most 1,728 rows: there
  * route_fused_packed splits K with partials in its workspace and this call
  * does not (the static scratch cannot hold them), so a value may differ in
- * the last bit, both within the same bounds. Every call on a GPU shares that
+ * the last bit, both within the same bounds, and such a call takes about as
+ * long as a 3072-row chunk. Every call on a GPU shares that
  * GPU's array, and the
  * decode counters carry over from call to call: two calls that overlap in
  * time on one GPU (different streams, threads or graphs running at once)
