@@ -106,3 +106,26 @@ def test_prefill_zero_rows_degenerate_case():
         assert np.array_equal(got["ids"][r], np.arange(16))
         assert (got["weights"][r] == np.float32(1.0 / 16.0)).all()
     check_outputs(xs, got, "prefill rows=200 with zero rows")
+
+
+@pytest.mark.parametrize("cap", [1, 100, 700])
+def test_prefill_plan_at_its_capacity(cap):
+    """Plans prepared for few rows size their workspace's K-split area for
+    their own capacity (14, 14 and 4 splits here): a call at the capacity
+    matches the oracle, packed and [K][N] alike, and the two agree bitwise."""
+    log(f"prefill plan of capacity {cap}, call at capacity")
+    w, wr = weights_dev(0)
+    xs = gen.hidden(cap, bank=650 + cap, outliers=True)
+    got = run_prefill(xs, cap=cap, fused=True)
+    check_outputs(xs, got, f"prefill cap={cap}")
+    plan = route.Plan(route.MODE_PREFILL, cap)
+    ws = plan.new_workspace()
+    pk = route.pack_weights(plan, w, wr)
+    o = Outputs(cap)
+    o.poison()
+    route.fused_packed(plan, bf16_dev(xs), pk, o.latent, o.logits, o.ids, o.weights, ws)
+    torch.cuda.synchronize()
+    h = o.host()
+    for k in ("latent", "ids"):
+        assert np.array_equal(h[k], got[k]), k
+    assert np.array_equal(h["logits"].view(np.uint32), got["logits"].view(np.uint32))
