@@ -10,10 +10,13 @@ the weights rotate over 8 distinct copies (8 x 77 MB, more than the 256 MB
 Infinity Cache) so every step streams its weights from HBM.
 
 Timing protocol (the pages time graph replays and report medians of
-repeated windows): the routes are replayed from HIP graphs, one holding a
-call per weight copy (each on its own input bank) and, when --steps is not a
-multiple of the copies, one holding the remaining calls, so a window runs
-exactly --steps routes. --warmup routes run untimed first; then the headline
+repeated windows): the routes are replayed from HIP graphs, one holding 25
+passes over the weight copies (200 calls, call i on copy i mod 8 with that
+copy's input bank) and, when --steps is not a multiple of that, one holding
+the remaining calls, so a window runs exactly --steps routes. Routes inside
+one graph run back to back like the layers of one decode step; the headline
+with one pass over the copies per graph (an extra graph boundary every 8
+routes, about 5 us each) is reported beside it as `graph8_us`. --warmup routes run untimed first; then the headline
 graph keeps replaying, untimed, for at least --clock-warmup-s seconds (the
 shader clock leaves its idle level only after about 0.2 s of load; reported
 on its own as `clock_warmup`). --windows windows of --steps routes are timed
@@ -61,6 +64,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "us per MoE-layer route (1-20 rows) + prefill rows/s; % HBM / MFMA peak"
 HBM_PEAK_GBPS = 8000.0
+# Decode graphs hold this many passes over the weight copies (200 routes for
+# 8 copies): routes inside one graph run back to back like the layers of a
+# decode step, while a graph boundary costs about 5 us of idle GPU (one graph
+# per pass over the 8 copies measured 18.17 us per 8-row route, graphs of 40
+# / 200 / 800 routes 17.57 / 17.49 / 17.47). The headline with one pass per
+# graph is reported beside it as `graph8_us`.
+GRAPH_CYCLES = 25
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 K, N, E = 7168, 3584, 896
 FIXED_BYTES = K * N * 2 + K * E * 4                       # 77,070,336
@@ -133,29 +143,35 @@ class DecodeSetup:
         self.copies = copies
 
     def run_all(self, count: int | None = None):
+        """`count` routes (default one per copy), call i on weight copy i mod
+        copies with that copy's input bank, outputs and workspace."""
         r = self.route
-        for i, (w, wr) in enumerate(self.copies[:count]):
+        n = len(self.copies)
+        for j in range(n if count is None else count):
+            i = j % n
+            w, wr = self.copies[i]
             r.fused(self.plan, self.xs[i], w, wr, self.lat[i], self.lg[i], self.ids[i], self.wt[i],
                     self.ws[i], rows=self.rows)
 
     def capture(self, count: int | None = None):
         return capture_graph(lambda: self.run_all(count), self.torch)
 
-    def runner(self, counts):
-        """A function that replays exactly n routes (n in `counts`): the graph
-        of one call per weight copy n // copies times, then a graph of the
-        first n % copies calls. Every graph is captured here, before any
-        timing."""
-        n_copies = len(self.copies)
-        full = self.capture()
-        part = {c % n_copies: self.capture(c % n_copies) for c in counts if c % n_copies}
+    def runner(self, counts, cycles: int = GRAPH_CYCLES):
+        """A function that replays exactly n routes (n in `counts`): a graph of
+        `cycles` passes over the weight copies, n // (cycles * copies) times,
+        then a graph of the remaining routes. Every graph is captured here,
+        before any timing."""
+        g_routes = cycles * len(self.copies)
+        full = self.capture(g_routes)
+        part = {c % g_routes: self.capture(c % g_routes) for c in counts if c % g_routes}
 
         def run(n: int):
-            for _ in range(n // n_copies):
+            for _ in range(n // g_routes):
                 full.replay()
-            if n % n_copies:
-                part[n % n_copies].replay()
+            if n % g_routes:
+                part[n % g_routes].replay()
         run.full = full
+        run.graph_routes = g_routes
         return run
 
 
@@ -170,9 +186,11 @@ class PackedDecodeSetup(DecodeSetup):
 
     def run_all(self, count: int | None = None):
         r = self.route
-        for i, pk in enumerate(self.packs[:count]):
-            r.fused_packed(self.plan, self.xs[i], pk, self.lat[i], self.lg[i], self.ids[i], self.wt[i],
-                           self.ws[i], rows=self.rows)
+        n = len(self.packs)
+        for j in range(n if count is None else count):
+            i = j % n
+            r.fused_packed(self.plan, self.xs[i], self.packs[i], self.lat[i], self.lg[i], self.ids[i],
+                           self.wt[i], self.ws[i], rows=self.rows)
 
 
 def time_routes(run, n: int, torch):
@@ -435,12 +453,14 @@ def main():
                 # the first graph: keep replaying (untimed) until the clock is up
                 t0 = time.perf_counter()
                 reps = 0
+                per = max(1, 400 // run.graph_routes)
                 while time.perf_counter() - t0 < args.clock_warmup_s:
-                    for _ in range(50):
+                    for _ in range(per):
                         run.full.replay()
-                    reps += 50
+                    reps += per
                     torch.cuda.synchronize()
-                clock_warm = {"seconds": round(time.perf_counter() - t0, 3), "routes": reps * copies_n,
+                clock_warm = {"seconds": round(time.perf_counter() - t0, 3),
+                              "routes": reps * run.graph_routes,
                               "note": "untimed replays of the headline graph after the warm-up routes"}
             windows = sorted(time_routes(run, steps, torch) for _ in range(args.windows))
             ms_win = windows[len(windows) // 2]
@@ -450,9 +470,15 @@ def main():
                 f"({decode_bytes(rows) / us / 1e3:.0f} GB/s; windows "
                 f"{', '.join(f'{w * 1000.0 / steps:.2f}' for w in windows)})")
             if rows == args.rows and name == "packed":
-                head = {"us": us, "ms_step": ms_win / steps,
+                head = {"us": us, "ms_step": ms_win / steps, "graph_routes": run.graph_routes,
                         "windows_us": [round(w * 1000.0 / steps, 3) for w in windows]}
-                clocks["decode"] = sample_sclk(lambda: [run.full.replay() for _ in range(25)], torch)
+                clocks["decode"] = sample_sclk(
+                    lambda: [run.full.replay() for _ in range(max(1, 200 // run.graph_routes))], torch)
+                # the same windows with one pass over the weight copies per graph
+                run1 = d.runner([steps], cycles=1)
+                w1 = sorted(time_routes(run1, steps, torch) for _ in range(args.windows))
+                head["graph8_us"] = round(w1[len(w1) // 2] * 1000.0 / steps, 3)
+                del run1
             del run, d
 
     us8 = head["us"]
@@ -586,9 +612,13 @@ def main():
             "weight_copies": copies_n,
             "weights": "packed once per copy by route_pack_weights, outside the timed region",
             "timing": f"median of {args.windows} windows of exactly {steps} route_fused_packed calls "
-                      f"replayed from HIP graphs, events on the launch stream",
+                      f"replayed from HIP graphs of {head['graph_routes']} calls ({GRAPH_CYCLES} passes "
+                      f"over the weight copies; fewer when the window is shorter), events on the launch "
+                      f"stream",
+            "graph_routes": head["graph_routes"],
         },
         "windows_us": head["windows_us"],
+        "graph8_us": head["graph8_us"],
         "clock_warmup": clock_warm,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -40,18 +40,29 @@ class _StubSetup(bench.DecodeSetup):
         self.replayed = []
 
     def capture(self, count=None):
-        return _StubGraph(self.replayed, len(self.copies[:count]))
+        return _StubGraph(self.replayed, len(self.copies) if count is None else count)
 
 
 def test_runner_replays_exactly_the_requested_routes():
     for copies in (1, 3, 8):
-        for steps, warm in ((1600, 80), (20, 5), (7, 0), (8, 8), (1, 1)):
-            d = _StubSetup(copies)
-            run = d.runner([steps, warm])
-            for n in (steps, warm):
-                d.replayed.clear()
-                run(n)
-                assert sum(d.replayed) == n, (copies, n)
-                # whole passes over the copies, then one shorter graph at most
-                assert all(c == copies for c in d.replayed[:n // copies])
-                assert len(d.replayed) == n // copies + (1 if n % copies else 0)
+        for cycles in (1, 25):
+            g = cycles * copies
+            for steps, warm in ((1600, 80), (20, 5), (7, 0), (8, 8), (1, 1), (200, 400)):
+                d = _StubSetup(copies)
+                run = d.runner([steps, warm], cycles=cycles)
+                assert run.graph_routes == g
+                for n in (steps, warm):
+                    d.replayed.clear()
+                    run(n)
+                    assert sum(d.replayed) == n, (copies, cycles, n)
+                    # whole graphs of `cycles` passes over the copies, then
+                    # one shorter graph at most
+                    assert all(c == g for c in d.replayed[:n // g])
+                    assert len(d.replayed) == n // g + (1 if n % g else 0)
+
+
+def test_default_graph_is_whole_passes_over_the_copies():
+    d = _StubSetup(8)
+    run = d.runner([1600])
+    assert run.graph_routes == bench.GRAPH_CYCLES * 8
+    assert 1600 % run.graph_routes == 0
