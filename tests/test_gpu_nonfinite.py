@@ -30,10 +30,15 @@ BF16_POS_INF, BF16_NEG_INF, BF16_NAN = 0x7F80, 0xFF80, 0x7FC0
 
 
 def poisoned_rows(rows: int, bank: int):
+    """Rows 1, 3, 5 and (from 18 rows) 17 and 19, whose decode router logits
+    run on the FP64 VALU at 17..20 rows; past 20 rows also the chunk's last
+    rows."""
     xs = gen.hidden(rows, bank=bank)
-    bad = {1: (100, BF16_POS_INF), 3: (5000, BF16_NEG_INF), 5: (7, BF16_NAN)}
+    bad = {1: (100, BF16_POS_INF), 3: (5000, BF16_NEG_INF), 5: (7, BF16_NAN),
+           17: (3000, BF16_NEG_INF), 19: (7100, BF16_NAN)}
     if rows > 20:
         bad.update({rows - 6: (7167, BF16_POS_INF), rows - 1: (0, BF16_NAN)})
+    bad = {r: kv for r, kv in bad.items() if r < rows}
     for r, (k, v) in bad.items():
         xs[r, k] = v
     return xs, sorted(bad)
@@ -86,7 +91,7 @@ def check_good_rows(got, ref, good, logits_ulp: bool):
 def test_decode_nonfinite_rows(packed):
     log(f"decode with inf / NaN hidden values, packed={packed}")
     w, wr = weights_dev(0)
-    for width in (8, 20):
+    for width in (4, 8, 20):
         xs, bad = poisoned_rows(width, bank=600 + width)
         plan = route.Plan(route.MODE_DECODE, width)
         ws = plan.new_workspace()
