@@ -234,10 +234,9 @@ int route_fused_packed(const route_plan* plan, const void* x, const void* packed
  * route_fused_packed splits K with partials in its workspace and this call
  * does not (the static scratch cannot hold them), so a value may differ in
  * the last bit, both within the same bounds, and such a call takes about as
- * long as a 3072-row chunk. Every call on a GPU shares that
- * GPU's array, and the
- * decode counters carry over from call to call: two calls that overlap in
- * time on one GPU (different streams, threads or graphs running at once)
+ * long as a 3072-row chunk. Every call on a GPU shares that GPU's array, and
+ * the decode counters carry over from call to call: two calls that overlap
+ * in time on one GPU (different streams, threads or graphs running at once)
  * race on it and must not be issued. Other statuses as route_fused_packed;
  * ROUTE_E_HIP if the array's address could not be taken for the device. */
 #define ROUTE_STATIC_SCRATCH_BYTES 3512832u
