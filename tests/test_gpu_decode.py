@@ -75,6 +75,16 @@ def test_decode_banks(width):
     assert decode_counters_idle(ws)
 
 
+@pytest.mark.parametrize("width", [w for w in range(1, 21) if w not in (1, 8, 9, 12, 16, 20)])
+def test_decode_other_widths(width):
+    """Every other call width of the 1..20 envelope, 10 banks each, fused
+    route on [K][N] weights against the oracle."""
+    log(f"decode parity width={width} banks=10")
+    xs, got, ws = run_banks(width, 10, fused=True)
+    check_outputs(xs, got, f"decode w={width}")
+    assert decode_counters_idle(ws)
+
+
 @pytest.mark.parametrize("width", list(range(1, 21)))
 def test_fused_equals_two_calls_bitwise(width):
     log(f"fused == latent_router + topk16, width={width}")

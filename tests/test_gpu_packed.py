@@ -103,6 +103,16 @@ def test_packed_decode_banks(width):
     assert decode_counters_idle(ws)
 
 
+@pytest.mark.parametrize("width", [2, 3, 6, 7, 10, 11, 13, 14, 15, 18, 19])
+def test_packed_decode_other_widths(width):
+    """Every other call width of the 1..20 envelope, 10 banks each, fused
+    route on packed weights against the oracle."""
+    log(f"packed decode parity width={width} banks=10")
+    xs, got, ws = run_packed_banks(width, 10, fused=True, seed=9000)
+    check_outputs(xs, got, f"packed decode w={width}")
+    assert decode_counters_idle(ws)
+
+
 @pytest.mark.parametrize("width", [1, 2, 4, 5, 8, 12, 13, 16, 17, 20])
 def test_packed_fused_equals_two_calls_bitwise(width):
     _, a, _ = run_packed_banks(width, 3, fused=True, seed=7500)
