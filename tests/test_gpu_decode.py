@@ -85,6 +85,35 @@ def test_decode_other_widths(width):
     assert decode_counters_idle(ws)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("width", [8, 20])
+def test_decode_outlier_channels(width, packed):
+    """Hidden rows with the prefill workload's outlier channels (1 % of the
+    channels scaled x20), where the FP32 accumulation of the latent has the
+    largest terms: 20 banks, fused route, both weight layouts."""
+    log(f"decode with outlier channels width={width} packed={packed}")
+    w, wr = weights_dev(0)
+    plan = route.Plan(route.MODE_DECODE, width)
+    ws = plan.new_workspace()
+    pk = route.pack_weights(plan, w, wr) if packed else None
+    banks = 20
+    xs = np.concatenate([gen.hidden(width, bank=3000 + 100 * width + b, outliers=True) for b in range(banks)])
+    xd = bf16_dev(xs)
+    out = Outputs(width * banks)
+    out.poison()
+    for b in range(banks):
+        s = slice(b * width, (b + 1) * width)
+        if packed:
+            route.fused_packed(plan, xd[s], pk, out.latent[s], out.logits[s], out.ids[s], out.weights[s], ws,
+                               rows=width)
+        else:
+            route.fused(plan, xd[s], w, wr, out.latent[s], out.logits[s], out.ids[s], out.weights[s], ws,
+                        rows=width)
+    torch.cuda.synchronize()
+    check_outputs(xs, out.host(), f"decode outliers w={width} packed={packed}")
+    assert decode_counters_idle(ws)
+
+
 @pytest.mark.parametrize("width", list(range(1, 21)))
 def test_fused_equals_two_calls_bitwise(width):
     log(f"fused == latent_router + topk16, width={width}")
