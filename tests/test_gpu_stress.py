@@ -10,7 +10,7 @@ afterwards.
 Cancelling set (same page, Description, numerics bullet, which compares the
 two accuracies on partials that cancel): 1024 rows whose two halves of K
 cancel; relative RMS of the latent against float64 stays <= 2.0e-3 through
-the decode and the prefill kernels."""
+the decode (both weight layouts) and the prefill kernels."""
 import numpy as np
 import pytest
 import torch
@@ -80,7 +80,7 @@ def test_graph_replay_with_new_banks_and_poisoned_outputs(width):
 
 @pytest.mark.timeout(600)
 def test_cancelling_partials_single_rounding():
-    log("cancel set: 1024 rows through decode (20-row calls) and prefill")
+    log("cancel set: 1024 rows through decode (20-row calls, and packed 20- and 4-row calls) and prefill")
     xs, wc = gen.cancel_set(1024)
     w = bf16_dev(wc)
     _, wr = weights_dev(0)
@@ -106,9 +106,23 @@ def test_cancelling_partials_single_rounding():
     torch.cuda.synchronize()
     pre = bits_host(out2.latent)
 
+    # packed decode weights: their launches split K 8 ways up to 4 rows and
+    # 4 ways above, so 20-row and 4-row calls take both
+    packed = route.pack_weights(dplan, w, wr)
+    pk = {}
+    for width in (20, 4):
+        o = Outputs(1024)
+        for s in range(0, 1024, width):
+            n = min(width, 1024 - s)
+            route.latent_router_packed(dplan, xd[s:s + n], packed, o.latent[s:s + n], o.logits[s:s + n], ws,
+                                       rows=n)
+        torch.cuda.synchronize()
+        pk[width] = bits_host(o.latent)
+
     terms = orc.latent_abs_terms(xs, wc)
     ref = orc.round_f64_to_bf16_bits(exact)
-    for tag, got in (("decode", dec), ("prefill", pre)):
+    for tag, got in (("decode", dec), ("prefill", pre), ("packed decode, 20-row calls", pk[20]),
+                     ("packed decode, 4-row calls", pk[4])):
         lc = compare.latent_check(got, ref, exact, terms)
         log(f"cancel {tag}: {lc} | two-round relRMS {rr_two:.4g}")
         assert lc["fail"] == 0
