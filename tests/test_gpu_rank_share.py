@@ -82,18 +82,22 @@ def check_outputs(xs, got_latent, got_logits, ref, tag):
 
 
 @pytest.mark.parametrize("ranks", RANKS)
-@pytest.mark.parametrize("width", [1, 8, 20])
+@pytest.mark.parametrize("width", [1, 4, 8, 16, 17, 20])
 def test_share_banks(ranks, width):
+    """40 banks at 1 / 8 / 20 rows, 10 at 4 / 16 / 17 (either side of the
+    16-row step where rows 16..19 of the router move to the VALU), each width
+    on another rank."""
     lat, exp = route.RANK_SHARES[ranks]
-    rank = {1: 0, 8: ranks - 1, 20: ranks // 2 + 1}[width]
-    log(f"share parity ranks={ranks} rank={rank} width={width} banks={BANKS}")
+    rank = {1: 0, 4: 1, 8: ranks - 1, 16: 2, 17: ranks - 2, 20: ranks // 2 + 1}[width]
+    banks = BANKS if width in (1, 8, 20) else 10
+    log(f"share parity ranks={ranks} rank={rank} width={width} banks={banks}")
     _, _, w, wr = share_weights(ranks, rank)
     plan = route.Plan(route.MODE_DECODE, width, latent=lat, experts=exp)
     ws = plan.new_workspace()
-    xs = np.concatenate([gen.hidden(width, bank=7000 + 100 * width + b) for b in range(BANKS)])
+    xs = np.concatenate([gen.hidden(width, bank=7000 + 100 * width + b) for b in range(banks)])
     xd = bf16_dev(xs)
     lat_h, lg_h = [], []
-    for b in range(BANKS):
+    for b in range(banks):
         o = ShareOutputs(width, lat, exp)
         route.latent_router(plan, xd[b * width:(b + 1) * width], w, wr, o.latent, o.logits, ws,
                             rows=width)
