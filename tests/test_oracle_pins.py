@@ -399,6 +399,40 @@ def test_comparator_ulp_helpers():
     assert c.bf16_spacing(np.uint16(0x0001)) == 2.0 ** -133
 
 
+def test_f32_spacing_against_numpy():
+    """The FP32 unit in the last place at a value (the logits band's
+    half-ULP term) equals numpy's spacing above |v|, for normals of every
+    exponent, powers of two, subnormals and zero, either sign."""
+    r = np.random.default_rng(5)
+    bits = r.integers(0, 0x7F800000, 4000, dtype=np.uint32)
+    v = np.concatenate([bits.view(np.float32),
+                        np.float32([0.0, 1.0, 2.0, 0.5, 3.0e38, np.finfo(np.float32).tiny,
+                                    np.finfo(np.float32).smallest_subnormal])])
+    v = np.concatenate([v, -v])
+    ref = np.abs(np.spacing(np.abs(v))).astype(np.float64)
+    assert np.array_equal(c.f32_spacing(v), ref)
+
+
+def test_weights_check_counts_ulps():
+    """Weights exactly 5 FP32 ULP away pass, 6 away fail (the window of the
+    weights criterion); signed zeros are equal; the counts and the largest
+    distance are reported."""
+    ref = np.float32([0.0625, 0.3, 1e-6, 0.0])
+    got = ref.copy()
+    for _ in range(5):
+        got[0] = np.nextafter(got[0], np.float32(1))
+        got[1] = np.nextafter(got[1], np.float32(-1))
+    got[3] = np.float32(-0.0)
+    r = c.weights_check(got, ref)
+    assert r == {"n": 4, "max_ulp": 5, "fail": 0}
+    got[2] = ref[2]
+    for _ in range(6):
+        got[2] = np.nextafter(got[2], np.float32(1))
+    r = c.weights_check(got, ref)
+    assert r["fail"] == 1 and r["max_ulp"] == 6
+    assert c.weights_check(got, ref, max_ulp=6)["fail"] == 0
+
+
 def test_latent_check_flags_a_wrong_value():
     x = g.hidden(2, bank=1)
     w = g.latent_weight(0)
