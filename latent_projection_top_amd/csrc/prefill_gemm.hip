@@ -52,6 +52,8 @@
 // instruction of the transposing read. Every lane receives the same operand
 // values in the same order as with the [K][N] weights, so the results are
 // bitwise the same.
+#include <type_traits>
+
 #include "route_device.h"
 #include "route_launch.h"
 
@@ -298,23 +300,25 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   const char* b_src = reinterpret_cast<const char*>(w);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-  auto issue_one = [&](int kt, int i) {
+  // `full`: this wave owns PER_WAVE loads of every stage (else PER_WAVE - 1);
+  // the pipeline below is instantiated for both, so no stage tests it
+  auto issue_one = [&](int kt, int i, bool full) {
     const uint32_t st = lds0 + (kt % kGStages) * S::STAGE;
     const char* ab = a_src + (size_t)kt * (kGBK * 2);
     const char* bb = b_src + (BT ? (size_t)kt * (kGBK * 2) : (size_t)kt * ((size_t)kGBK * S::N * 2));
     const int c = wave + kGWaves * i;
     if (i < kAW)
       dma16(ab, off[i], st + c * 1024);
-    else if (c < S::LOADS) {
+    else if (i < S::PER_WAVE - 1 || full) {
       if constexpr (BT)
         dma16(bb + (size_t)(i - kAW) * kBtStep, off[kAW], st + c * 1024);
       else
         dma16(bb, off[i], st + c * 1024);
     }
   };
-  auto issue = [&](int kt) {
+  auto issue = [&](int kt, bool full) {
 #pragma unroll
-    for (int i = 0; i < S::PER_WAVE; ++i) issue_one(kt, i);
+    for (int i = 0; i < S::PER_WAVE; ++i) issue_one(kt, i, full);
   };
 
   // ---- LDS -> register operand addresses ----------------------------------
@@ -384,7 +388,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   // with the next K half's value as soon as its last MFMA has been issued
   // (a[i] after row i, b[j] in the last row), so the next half's operands
   // arrive while this half's MFMAs run, without a second register set.
-  auto step = [&](Ops& o, bool restart, bool reload, uint32_t st_n, int s_n, int dma_kt) {
+  auto step = [&](Ops& o, bool restart, bool reload, uint32_t st_n, int s_n, int dma_kt, bool dma, bool full) {
 #pragma unroll
     for (int i = 0; i < S::MT; ++i) {
 #pragma unroll
@@ -394,7 +398,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
           // goes out after MFMA kEvery * d + 1
           constexpr int kEvery = (S::MT * S::NT) / S::PER_WAVE;
           const int p = i * S::NT + j;
-          if (dma_kt >= 0 && p % kEvery == 1 && p / kEvery < S::PER_WAVE) issue_one(dma_kt, p / kEvery);
+          if (dma && p % kEvery == 1 && p / kEvery < S::PER_WAVE) issue_one(dma_kt, p / kEvery, full);
         }
         if constexpr (Router) {
           const int c = j < 2 ? j : 2 + (j & 1);
@@ -417,51 +421,69 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   // meets the others at the barrier: past it, stage kt + 1 is complete in
   // LDS and stage kt's buffer takes the loads of stage kt + 3, while the
   // second half runs and reads the first half of stage kt + 1.
-  issue(kt0);
-  issue(kt0 + 1);
-  issue(kt0 + 2);
-  if (Router && tid < kGBM / 64) bad_rows[tid] = 0;
-  vm_wait_stages<S::PER_WAVE>(full_wave, 2);
-  __syncthreads();
-  Ops o;
+  // The pipeline is instantiated for full and short waves (a wave-uniform
+  // choice made once), so that no stage branches on it.
+  auto pipeline = [&](auto full_tag) {
+    constexpr bool kFull = decltype(full_tag)::value;
+    issue(kt0, kFull);
+    issue(kt0 + 1, kFull);
+    issue(kt0 + 2, kFull);
+    if (Router && tid < kGBM / 64) bad_rows[tid] = 0;
+    vm_wait_stages<S::PER_WAVE>(kFull, 2);
+    __syncthreads();
+    Ops o;
 #pragma unroll
-  for (int i = 0; i < S::MT; ++i) o.a[i] = read_a(stage_lds(kt0), 0, i);
+    for (int i = 0; i < S::MT; ++i) o.a[i] = read_a(stage_lds(kt0), 0, i);
 #pragma unroll
-  for (int j = 0; j < S::NT; ++j) o.b[j] = read_b(stage_lds(kt0), 0, j);
+    for (int j = 0; j < S::NT; ++j) o.b[j] = read_b(stage_lds(kt0), 0, j);
 
-#pragma unroll 1
-  for (int kp = kt0; kp < kend; kp += kGFoldStages) {
+    // One fold period (kGFoldStages stages). Every period but the last has the
+    // loads of the next two stages in flight at each wait and issues the loads
+    // of stage kt + 3; the last period (Tail) drains them. With the tail
+    // peeled, the steady-state stages carry no run-time conditions.
+    auto period = [&](int kp, auto tail) {
+      constexpr bool kTail = decltype(tail)::value;
 #pragma unroll
-    for (int u = 0; u < kGFoldStages; ++u) {
-      const int kt = kp + u;
-      step(o, u == 0, true, stage_lds(kt), 1, -1);
-      lgkm_wait0();
-      vm_wait_stages<S::PER_WAVE>(full_wave, kt + 2 < kend ? 1 : 0);
-      __syncthreads();
-      // (after the last stage this reads a stale buffer; the values go unused)
-      // Stage kt + 3's loads: the router GEMM spreads them over the second
-      // half's MFMAs so that the matrix core restarts right after the
-      // barrier (measured: latent + router 239.9 against 245.8 us, 4
-      // interleaved pairs); the latent GEMM issues them together, because
-      // spreading them there spills 42 registers.
-      if (!Router && kt + 3 < kend) issue(kt + 3);
-      step(o, false, true, stage_lds(kt + 1), 0, Router && kt + 3 < kend ? kt + 3 : -1);
-    }
-    // fold the restarted chains into the long sums
-#pragma unroll
-    for (int i = 0; i < S::MT; ++i) {
-      if constexpr (Router) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            sum64[i][j][t] += (double)chain[i][j][t] + (double)chain[i][j + 2][t];
-      } else {
-#pragma unroll
-        for (int j = 0; j < S::NT; ++j) sum32[i][j] += chain[i][j];
+      for (int u = 0; u < kGFoldStages; ++u) {
+        const int kt = kp + u;
+        step(o, u == 0, true, stage_lds(kt), 1, -1, false, kFull);
+        lgkm_wait0();
+        // (tail: kend - kp == kGFoldStages, so kt + 2 < kend is u < 2)
+        vm_wait_stages<S::PER_WAVE>(kFull, !kTail || u < kGFoldStages - 2 ? 1 : 0);
+        __syncthreads();
+        // (after the last stage this reads a stale buffer; the values go unused)
+        // Stage kt + 3's loads: spread over the second half's MFMAs, so that
+        // the matrix core restarts right after the barrier (router GEMM,
+        // measured: latent + router 239.9 against 245.8 us; packed latent
+        // GEMM 135.5 against 141.7 us), except in the [K][N] latent GEMM,
+        // which issues them together because spreading them there spills.
+        const bool more = !kTail || u < kGFoldStages - 3;   // kt + 3 < kend
+        if (!Router && !BT && more) issue(kt + 3, kFull);
+        step(o, false, true, stage_lds(kt + 1), 0, kt + 3, (Router || BT) && more, kFull);
       }
-    }
-  }
+      // fold the restarted chains into the long sums
+#pragma unroll
+      for (int i = 0; i < S::MT; ++i) {
+        if constexpr (Router) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              sum64[i][j][t] += (double)chain[i][j][t] + (double)chain[i][j + 2][t];
+        } else {
+#pragma unroll
+          for (int j = 0; j < S::NT; ++j) sum32[i][j] += chain[i][j];
+        }
+      }
+    };
+#pragma unroll 1
+    for (int kp = kt0; kp < kend - kGFoldStages; kp += kGFoldStages) period(kp, std::false_type{});
+    period(kend - kGFoldStages, std::true_type{});
+  };
+  if (full_wave)
+    pipeline(std::true_type{});
+  else
+    pipeline(std::false_type{});
 
   // lane (g, m) of tile (i, j) holds row 16 i + 4 g + t, column 16 j + m
   if (part != nullptr) {
