@@ -453,13 +453,11 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
         __syncthreads();
         // (after the last stage this reads a stale buffer; the values go unused)
         // Stage kt + 3's loads: spread over the second half's MFMAs, so that
-        // the matrix core restarts right after the barrier (router GEMM,
-        // measured: latent + router 239.9 against 245.8 us; packed latent
-        // GEMM 135.5 against 141.7 us), except in the [K][N] latent GEMM,
-        // which issues them together because spreading them there spills.
+        // the matrix core restarts right after the barrier (measured: latent
+        // + router 239.9 against 245.8 us; packed latent GEMM 135.5 against
+        // 141.7 us; [K][N] latent GEMM 130.3-131.0 against 143.1-146.1 us).
         const bool more = !kTail || u < kGFoldStages - 3;   // kt + 3 < kend
-        if (!Router && !BT && more) issue(kt + 3, kFull);
-        step(o, false, true, stage_lds(kt + 1), 0, kt + 3, (Router || BT) && more, kFull);
+        step(o, false, true, stage_lds(kt + 1), 0, kt + 3, more, kFull);
       }
       // fold the restarted chains into the long sums
 #pragma unroll
