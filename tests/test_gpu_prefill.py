@@ -70,16 +70,17 @@ def test_prefill_chunk_3072_outliers(bank):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("rows", [1, 77, 130, 191, 192, 193, 384, 700, 768, 769, 1000, 1536, 1537, 1700,
-                                  1729, 3071])
+                                  1729, 2048, 2500, 2880, 3071])
 def test_prefill_ragged(rows):
     """Row counts around the 192-row block tile and across the K splits of
     chunks with few row tiles: one row, a partial first tile, one row short
     of a tile, a whole tile (14 splits), one row into the second tile and two
     whole tiles (7), four tiles (4), six tiles (2), nine tiles (the router
-    alone split in 2), and one row short of the largest chunk (unsplit).
-    Each change of split is tested on both sides: 768 / 769 rows (4 ways,
-    then 2), 1,536 / 1,537 (both GEMMs in 2, then the router alone) and
-    1,700 / 1,729 (the router in 2, then neither)."""
+    alone split in 2), then 10 to 16 row tiles (unsplit, fewer tiles than
+    CUs: 11, 14, 15 and 16 here). Each change of split is tested on both
+    sides: 768 / 769 rows (4 ways, then 2), 1,536 / 1,537 (both GEMMs in 2,
+    then the router alone) and 1,700 / 1,729 (the router in 2, then
+    neither)."""
     log(f"prefill ragged rows={rows}")
     xs = gen.hidden(rows, bank=600 + rows, outliers=True)
     got = run_prefill(xs, cap=3072)
