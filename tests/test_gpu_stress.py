@@ -355,3 +355,62 @@ def test_prefill_graph_replay(packed):
         call(banks[(b + 1) % nb], spare)
         torch.cuda.synchronize()
     assert mismatches == 0
+
+
+@pytest.mark.timeout(600)
+def test_prefill_graph_replay_full_and_split_chunks():
+    """Full-size prefill calls sharing one workspace in one HIP graph: a
+    packed 3072-row chunk (both GEMMs unsplit, then the top-16), a packed
+    1024-row chunk (both GEMMs split in 2 along K, each followed by its
+    combine kernel) and a 3072-row chunk on [K][N] weights (the router
+    weight split on every call), each after poisoning its outputs. Every
+    replay takes a new bank of hidden rows and must equal the eager result
+    for that bank bit for bit."""
+    w, wr = weights_dev(0)
+    plan = route.Plan(route.MODE_PREFILL, 3072)
+    ws = plan.new_workspace()
+    packed = route.pack_weights(plan, w, wr)
+    nb = 3
+    banks = [bf16_dev(gen.hidden(3072, bank=21000 + b, outliers=True)) for b in range(nb)]
+
+    def run(x, outs):
+        big, small, kn = outs
+        for o in outs:
+            o.poison()
+        route.fused_packed(plan, x, packed, big.latent, big.logits, big.ids, big.weights, ws)
+        route.fused_packed(plan, x[:1024], packed, small.latent, small.logits, small.ids, small.weights, ws,
+                           rows=1024)
+        route.fused(plan, x, w, wr, kn.latent, kn.logits, kn.ids, kn.weights, ws)
+
+    refs = []
+    for b in range(nb):
+        outs = (Outputs(3072), Outputs(1024), Outputs(3072))
+        run(banks[b], outs)
+        refs.append(outs)
+    torch.cuda.synchronize()
+
+    x_static = torch.empty_like(banks[0])
+    x_static.copy_(banks[0])
+    outs = (Outputs(3072), Outputs(1024), Outputs(3072))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(x_static, outs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(x_static, outs)
+    torch.cuda.synchronize()
+
+    for i in range(12):
+        b = (i * 2 + 1) % nb
+        log(f"prefill graph replay {i} bank {b}")
+        x_static.copy_(banks[b])
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(outs, refs[b]):
+            assert torch.equal(got.latent, ref.latent), i
+            assert torch.equal(got.logits.view(torch.int32), ref.logits.view(torch.int32)), i
+            assert torch.equal(got.ids, ref.ids), i
+            assert torch.equal(got.weights.view(torch.int32), ref.weights.view(torch.int32)), i
