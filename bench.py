@@ -537,7 +537,7 @@ def main():
             lambda: [route.latent_router_packed(plan, x, packed, lat, lg, ws) for _ in range(10)], torch)
         t_all_kn = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr_kn = t_call(lambda: route.latent_router(plan, x, w0, wr0, lat, lg, ws), args.prefill_reps)
-        # the pages' other chunk size: 1024 rows (6 row tiles, K split in 2)
+        # the pages' other chunk size: 1024 rows (8 row tiles of 128 rows, K split in 2)
         t_1024 = t_call(lambda: route.fused_packed(plan, x[:1024], packed, lat[:1024], lg[:1024], ids[:1024],
                                                    wt[:1024], ws, rows=1024), args.prefill_reps)
         del packed, p
@@ -565,7 +565,7 @@ def main():
             "chunk_1024": {"rows": 1024, "us_per_chunk": round(t_1024, 2),
                            "rows_per_s": round(1024 / (t_1024 * 1e-6)),
                            "note": "packed weights, the same plan; chunks of 1..1728 rows split K over more "
-                                   "workgroups (1024 rows: 2 splits)"},
+                                   "workgroups (1024 rows: 2 splits, 128-row block tiles)"},
         }
         log(f"prefill 3072 (packed): {t_all:.1f} us ({prefill['rows_per_s']:.3g} rows/s), projection "
             f"{t_lr:.1f} us = {prefill['method_tflops']} TFLOP/s of the method's work "

@@ -27,8 +27,9 @@
 // Tiling for gfx950 (256 CUs): block tile 192 rows x 224 columns (latent) or
 // 192 x 192 (router: 64 experts x 3 parts), so 3072 rows give 256 latent
 // blocks, one per CU; chunks of few row tiles also split K over more blocks
-// (prefill_splits). Eight waves, 4 x 2, each 48 rows x (112 | 96) columns
-// with its accumulators in VGPRs: two waves per SIMD keep the matrix core
+// (prefill_splits), and some chunk sizes take 128-row tiles instead
+// (prefill_gemm_plan). Eight waves, 4 x 2, each 48 (or 32) rows x (112 | 96)
+// columns with its accumulators in VGPRs: two waves per SIMD keep the matrix core
 // busy where one wave holding everything in AGPRs reaches only about 55% of
 // its rate. K step 64, three LDS stages (156 KB at most). Operands go from global
 // memory straight to LDS (global_load_lds_dwordx4: 64 lanes x 16 bytes land
@@ -59,7 +60,7 @@
 
 namespace route {
 
-constexpr int kGBM = 192;
+constexpr int kGBM = 192;             // rows of a block tile (or 128, below)
 constexpr int kGBK = 64;
 constexpr int kGStages = 3;
 constexpr int kGWaves = 8;
@@ -75,14 +76,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <bool Router>
+template <bool Router, int BMr>
 struct GemmShape {
+  static constexpr int BM = BMr;                     // block rows: 192, or 128
   static constexpr int BN = Router ? 192 : 224;      // block columns
   static constexpr int NT = Router ? 6 : 7;          // 16-column MFMA tiles per wave
-  static constexpr int MT = 3;                       // 16-row MFMA tiles per wave
+  static constexpr int MT = BM / 64;                 // 16-row MFMA tiles per wave (4 row slices)
   static constexpr int NB = BN / 32;                 // 32-column B blocks per stage
   static constexpr int N = Router ? kRouterCols : kLatent;
-  static constexpr int A_BYTES = kGBM * kGBK * 2;    // 24576
+  static constexpr int A_BYTES = BM * kGBK * 2;      // 24576 or 16384
   static constexpr int B_BYTES = NB * kGBK * 64;     // NB x 4096
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024;     // 1 KB loads per stage (block)
@@ -91,6 +93,7 @@ struct GemmShape {
   static constexpr int PER_WAVE = (LOADS + kGWaves - 1) / kGWaves;
   static_assert(N % BN == 0, "column tiles");
   static_assert(A_LOADS % kGWaves == 0, "A loads come first and split evenly");
+  static_assert(BM == 192 || BM == 128, "block rows");
   static_assert(kGStages * STAGE <= 160 * 1024, "LDS");
 };
 
@@ -166,16 +169,16 @@ __device__ __forceinline__ bool f32_nonfinite(float v) {
 // in a fixed order and rounded once to FP32; finite logits keep the GEMM's
 // value. mask[b] bit j: row bm0 + 64 b + j holds a non-finite logit of the
 // tile. red: 256 doubles of LDS.
-template <bool BT>
+template <bool BT, int NW>
 __device__ void router_recompute(const uint16_t* __restrict__ x, const uint16_t* __restrict__ parts,
-                                 float* __restrict__ logits, int bm0, int group, const uint64_t (&mask)[kGBM / 64],
+                                 float* __restrict__ logits, int bm0, int group, const uint64_t (&mask)[NW],
                                  double* red) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int e = group * 64 + lane;
   const int kb = (wave & 3) * (kHidden / 4);
 #pragma unroll 1
-  for (int b = 0; b < kGBM / 64; ++b) {
+  for (int b = 0; b < NW; ++b) {
     uint64_t todo = mask[b];
     while (todo != 0) {
       const int r = bm0 + 64 * b + __builtin_ctzll(todo);
@@ -223,22 +226,22 @@ __device__ void router_recompute(const uint16_t* __restrict__ x, const uint16_t*
   }
 }
 
-template <bool Router, bool BT>
+template <bool Router, bool BT, int BM>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                          void* __restrict__ out, int rows, int mtiles, int nsplit, void* __restrict__ part) {
-  using S = GemmShape<Router>;
+  using S = GemmShape<Router, BM>;
   __shared__ __attribute__((aligned(1024))) char smem[kGStages * S::STAGE];
   // router: rows of the tile with a non-finite logit (bit j of word b: row
   // bm0 + 64 b + j)
-  __shared__ uint64_t bad_rows[Router ? kGBM / 64 : 1];
+  __shared__ uint64_t bad_rows[Router ? BM / 64 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int m = lane & 15;
-  const int wm = wave >> 1;  // 48-row slice
+  const int wm = wave >> 1;  // 16 MT-row slice
   const int wn = wave & 1;   // column half
 
   // Tile order. The hardware deals blocks round-robin over the 8 XCDs, so
@@ -262,7 +265,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   const int first = grp * 8;
   const int gm = min(mtiles - first, 8);
   const int loc = lin - grp * 8 * ntiles;
-  const int bm0 = (first + loc % gm) * kGBM;
+  const int bm0 = (first + loc % gm) * BM;
   const int bn0 = (loc / gm) * S::BN;
 
   // ---- global -> LDS loads: load c of a stage (wave c % 8) -----------------
@@ -322,13 +325,13 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   };
 
   // ---- LDS -> register operand addresses ----------------------------------
-  // A, tile i, K half s: row 48 wm + 16 i + m, piece 4 s + g (the swizzle
-  // term (row >> 1) & 7 equals (m >> 1) & 7 because 48 wm + 16 i is a
+  // A, tile i, K half s: row 16 MT wm + 16 i + m, piece 4 s + g (the swizzle
+  // term (row >> 1) & 7 equals (m >> 1) & 7 because 16 MT wm + 16 i is a
   // multiple of 16).
   uint32_t a_rd[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
-    a_rd[s] = (uint32_t)((48 * wm + m) * 128 + (((4 * s + g) ^ ((m >> 1) & 7)) * 16));
+    a_rd[s] = (uint32_t)((16 * S::MT * wm + m) * 128 + (((4 * s + g) ^ ((m >> 1) & 7)) * 16));
   // B, 16-column half h of a 32-column block, K rows 8 g + m / 4 (+ 32 s + 4 e),
   // columns 16 h + 4 (m % 4) .. + 3.
   uint32_t b_rd[2];
@@ -428,7 +431,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     issue(kt0, kFull);
     issue(kt0 + 1, kFull);
     issue(kt0 + 2, kFull);
-    if (Router && tid < kGBM / 64) bad_rows[tid] = 0;
+    if (Router && tid < BM / 64) bad_rows[tid] = 0;
     vm_wait_stages<S::PER_WAVE>(kFull, 2);
     __syncthreads();
     Ops o;
@@ -490,7 +493,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     for (int i = 0; i < S::MT; ++i) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int row = bm0 + 48 * wm + 16 * i + 4 * g + t;
+        const int row = bm0 + 16 * S::MT * wm + 16 * i + 4 * g + t;
         if (row >= rows) continue;
         if constexpr (Router) {
           const int e0 = (bn0 / 192) * 64 + 32 * wn + m;
@@ -511,7 +514,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   for (int i = 0; i < S::MT; ++i) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = bm0 + 48 * wm + 16 * i + 4 * g + t;
+      const int row = bm0 + 16 * S::MT * wm + 16 * i + 4 * g + t;
       if (row >= rows) continue;
       if constexpr (Router) {
         // expert group bn0 / 192, experts 32 wn + 16 j + m of its 64
@@ -538,13 +541,14 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   }
   if constexpr (Router) {
     __syncthreads();
-    uint64_t mask[kGBM / 64];
+    uint64_t mask[BM / 64];
     uint64_t any = 0;
 #pragma unroll
-    for (int b = 0; b < kGBM / 64; ++b) any |= (mask[b] = bad_rows[b]);
+    for (int b = 0; b < BM / 64; ++b) any |= (mask[b] = bad_rows[b]);
     // (every stage's reads are done: the LDS stages are free)
     if (any != 0)
-      router_recompute<BT>(x, w, static_cast<float*>(out), bm0, bn0 / 192, mask, reinterpret_cast<double*>(smem));
+      router_recompute<BT, BM / 64>(x, w, static_cast<float*>(out), bm0, bn0 / 192, mask,
+                                    reinterpret_cast<double*>(smem));
   }
 }
 
@@ -563,12 +567,60 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
 // of K rounded once: the combine adds the splits' FP32 (latent) or FP64
 // (router) sums in split order in FP64. The split changes the order of the
 // FP32 additions, so a row's last bit may depend on the chunk's row count.
-int prefill_splits(int mtiles, bool router) {
+static int prefill_splits(int mtiles, bool router) {
   if (mtiles <= 1) return 14;
   if (mtiles == 2) return 7;
   if (mtiles <= 4) return 4;
   if (mtiles <= 8 || (router && mtiles == 9)) return 2;
   return 1;
+}
+
+// Row tiles of 128 instead of 192 rows (same waves, 32-row wave tiles) fill
+// the CUs better at some row counts (1024 rows: 8 x 16 x 2 = 256 latent
+// blocks, where 192-row tiles give 6 x 16 x 2 = 192 and leave most of the
+// last tile empty), at a higher cost per output (measured at 1024 rows, K
+// split in 2, one box: packed latent GEMM 54.1-54.6 against 63.4-63.5 us,
+// router 49.6-50.2 against 55.2, for 2/3 of the work per block: 1.28 and
+// 1.36 times the cost per output). A call takes 128-row tiles, with the K
+// split that suits them, where a model of the GEMM's time predicts them 5 %
+// faster than the 192-row plan above: rounds of 256 blocks times one
+// block's time (its rows x K stages at the measured cost of its tile
+// height; a 192-row block over the full K takes about 127 us in the latent
+// GEMM and 105 in the router's) plus the combine pass of a K split (its
+// partials at the combine kernels' measured rates). Every output is the
+// same sum in the same order whatever the tile height; only the K split
+// changes the order of the additions.
+struct GemmPlan {
+  int bm;  // block rows
+  int ns;  // K splits
+};
+
+static double gemm_model_us(int rows, bool router, int bm, int ns) {
+  const int nt = router ? kRouterCols / 192 : kLatent / 224;
+  const double full_us = router ? 105.0 : 127.0;                   // 192-row block, full K
+  const double per_out = bm == 192 ? 1.0 : (router ? 1.36 : 1.28);  // cost per output, relative
+  const int blocks = (rows + bm - 1) / bm * nt * ns;
+  const int rounds = (blocks + 255) / 256;
+  double t = rounds * full_us * (bm / 192.0) * per_out / ns;
+  if (ns > 1)
+    t += router ? 1.0 + ns * (double)rows * kExperts * 8 / 3.5e6
+                : 1.0 + (ns * (double)rows * kLatent * 4 + (double)rows * kLatent * 2) / 5.2e6;
+  return t;
+}
+
+static GemmPlan prefill_gemm_plan(int rows, bool router, bool can_split) {
+  const GemmPlan base{kGBM, can_split ? prefill_splits((rows + kGBM - 1) / kGBM, router) : 1};
+  GemmPlan best = base;
+  double t_best = 0.95 * gemm_model_us(rows, router, base.bm, base.ns);
+  for (const int ns : {1, 2, 4, 7, 14}) {
+    if (ns > 1 && !can_split) break;
+    const double t = gemm_model_us(rows, router, 128, ns);
+    if (t < t_best) {
+      best = GemmPlan{128, ns};
+      t_best = t;
+    }
+  }
+  return best;
 }
 
 // Latent combine: latent[r][n] = BF16(sum over splits of part[q][r][n]), the
@@ -645,8 +697,8 @@ __global__ __launch_bounds__(256) void router_combine_kernel(const double* __res
     atomicOr((unsigned long long*)&bad_rows, (unsigned long long)mine);
   }
   __syncthreads();
-  const uint64_t mask[kGBM / 64] = {bad_rows, 0ull, 0ull};
-  if (mask[0] != 0) router_recompute<BT>(x, parts_w, logits, r0, e0 / 64, mask, red);
+  const uint64_t mask[1] = {bad_rows};
+  if (mask[0] != 0) router_recompute<BT, 1>(x, parts_w, logits, r0, e0 / 64, mask, red);
 }
 
 // The three exact BF16 parts of an FP32 weight: each takes the top 8
@@ -742,9 +794,8 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // FP32 and the router GEMM's FP64 sums per split, one after the other in
 // time, so they share one area.
 static size_t split_part_bytes(int rows) {
-  const int mt = (rows + kGBM - 1) / kGBM;
-  const int sl = prefill_splits(mt, false);
-  const int sr = prefill_splits(mt, true);
+  const int sl = prefill_gemm_plan(rows, false, true).ns;
+  const int sr = prefill_gemm_plan(rows, true, true).ns;
   const size_t lat = sl > 1 ? (size_t)sl * rows * kLatent * sizeof(float) : 0;
   const size_t rt = sr > 1 ? (size_t)sr * rows * kExperts * sizeof(double) : 0;
   return lat > rt ? lat : rt;
@@ -759,27 +810,25 @@ size_t prefill_workspace_bytes(int rows_cap, size_t* off_logits, size_t* off_par
   *off_cand = off;
   off += align256(sizeof(uint64_t) * (size_t)rows_cap * kTopkMaxShards * kTopK);
   *off_split = off;
-  // the largest split area over every row count the plan accepts (it peaks
-  // at the last row of some row tile)
+  // the largest split area over every row count the plan accepts
   size_t most = 0;
-  for (int mt = 1; mt * kGBM - kGBM < rows_cap; ++mt) {
-    const size_t b = split_part_bytes(mt * kGBM < rows_cap ? mt * kGBM : rows_cap);
+  for (int r = 1; r <= rows_cap; ++r) {
+    const size_t b = split_part_bytes(r);
     most = b > most ? b : most;
   }
   return off + align256(most);
 }
 
-// One GEMM over `rows` rows, K-split when `part` is given and the row tiles
-// are few, then the combine of the split sums.
-template <bool Router, bool BT>
-static hipError_t launch_gemm(const uint16_t* x, const uint16_t* w, void* out, int rows, void* part,
-                              hipStream_t stream) {
-  using S = GemmShape<Router>;
-  const int mt = (rows + kGBM - 1) / kGBM;
-  const int ns = part != nullptr ? prefill_splits(mt, Router) : 1;
+// One GEMM over `rows` rows with `ns` K splits and `BM`-row tiles, then the
+// combine of the split sums.
+template <bool Router, bool BT, int BM>
+static hipError_t launch_gemm_tiles(const uint16_t* x, const uint16_t* w, void* out, int rows, int ns,
+                                    void* part, hipStream_t stream) {
+  using S = GemmShape<Router, BM>;
+  const int mt = (rows + BM - 1) / BM;
   const int blocks = mt * (S::N / S::BN) * ns;
-  hipError_t e = launch_kernel(prefill_gemm_kernel<Router, BT>, dim3(blocks), dim3(kGThreads), stream, x, w, out,
-                               rows, mt, ns, ns > 1 ? part : nullptr);
+  hipError_t e = launch_kernel(prefill_gemm_kernel<Router, BT, BM>, dim3(blocks), dim3(kGThreads), stream, x, w,
+                               out, rows, mt, ns, ns > 1 ? part : nullptr);
   if (e != hipSuccess || ns == 1) return e;
   if constexpr (Router) {
     const dim3 grid((rows + kCombRows - 1) / kCombRows, kExperts / 64);
@@ -804,6 +853,16 @@ static hipError_t launch_gemm(const uint16_t* x, const uint16_t* w, void* out, i
       default: return hipErrorInvalidValue;
     }
   }
+}
+
+// One GEMM over `rows` rows, K-split when `part` is given and the row tiles
+// are few, with the tile height and split of prefill_gemm_plan.
+template <bool Router, bool BT>
+static hipError_t launch_gemm(const uint16_t* x, const uint16_t* w, void* out, int rows, void* part,
+                              hipStream_t stream) {
+  const GemmPlan p = prefill_gemm_plan(rows, Router, part != nullptr);
+  return p.bm == 128 ? launch_gemm_tiles<Router, BT, 128>(x, w, out, rows, p.ns, part, stream)
+                     : launch_gemm_tiles<Router, BT, 192>(x, w, out, rows, p.ns, part, stream);
 }
 
 static_assert(kGKT % (28 * kGFoldStages) == 0, "every split of the K stages is whole fold periods");
