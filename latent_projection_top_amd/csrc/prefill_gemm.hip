@@ -29,11 +29,11 @@
 // blocks, one per CU; chunks of few row tiles also split K over more blocks
 // (prefill_splits), and some chunk sizes take 128-row tiles instead
 // (prefill_gemm_plan). Eight waves, 4 x 2, each 48 (or 32) rows x (112 | 96)
-// columns with its accumulators in VGPRs: two waves per SIMD keep the matrix core
-// busy where one wave holding everything in AGPRs reaches only about 55% of
-// its rate. K step 64, three LDS stages (156 KB at most). Operands go from global
-// memory straight to LDS (global_load_lds_dwordx4: 64 lanes x 16 bytes land
-// contiguously), so no staging registers are spent on them:
+// columns with its accumulators in VGPRs: two waves per SIMD keep the matrix
+// core busy where one wave holding everything in AGPRs reaches only about 55%
+// of its rate. K step 64, three LDS stages (156 KB at most). Operands go from
+// global memory straight to LDS (global_load_lds_dwordx4: 64 lanes x 16
+// bytes land contiguously), so no staging registers are spent on them:
 //   A stage [192 rows][64 k]: 128-byte rows, the 16-byte piece c of row r
 //     stored at position c ^ ((r >> 1) & 7), so the 16 rows one MFMA lane
 //     group reads hit 16 different bank groups;
@@ -241,7 +241,7 @@ void prefill_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int m = lane & 15;
-  const int wm = wave >> 1;  // 16 MT-row slice
+  const int wm = wave >> 1;  // row slice (16 MT rows)
   const int wn = wave & 1;   // column half
 
   // Tile order. The hardware deals blocks round-robin over the 8 XCDs, so
