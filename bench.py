@@ -510,9 +510,10 @@ def main():
 
         def t_call(fn, reps):
             # the first calls after the decode phase run slower (clocks rise
-            # under the compute-bound GEMMs): warm up for about 12 ms, then
-            # take the median of five timed windows
-            for _ in range(40):
+            # under the compute-bound GEMMs for about 25 ms of 3072-row
+            # chunks): warm up for 120 calls, then take the median of five
+            # timed windows
+            for _ in range(120):
                 fn()
             torch.cuda.synchronize()
             times = []
