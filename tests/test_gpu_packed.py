@@ -231,3 +231,32 @@ def test_prefill_packed_bitwise_equal_to_unpacked(rows):
         lc = compare.latent_check(g["latent"], ref_o["latent"], ref_o["exact"], ref_o["abs_terms"])
         ic = compare.ids_check(g["ids"], ref_o["ids"], ref_o["logits"])
         assert lc["fail"] == 0 and ic["violations"] == 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rows", [128, 129, 256, 257, 512, 513, 1024, 1025, 1152, 1153, 2049, 2304, 2305])
+def test_prefill_tile_plan_boundaries(rows):
+    """Both sides of every change between 128- and 192-row block tiles in
+    the prefill plan (the latent GEMM switches at 128 / 192 / 256 / 384 /
+    512 / 768 / 1024 / 1536 / 2048 rows, the router at 128 / 192 / 256 /
+    384 / 512 / 768 / 1152 / 1728 / 2304): the packed call against the
+    oracle, and bitwise against the [K][N] call, which takes the same plan."""
+    from tests.test_gpu_prefill import check_outputs
+    w, wr = weights_dev(0)
+    plan, packed = prefill_packed(0)
+    xs = gen.hidden(rows, bank=8600 + rows, outliers=True)
+    xd = bf16_dev(xs)
+    ws = plan.new_workspace()
+    ref, got = Outputs(rows), Outputs(rows)
+    for o in (ref, got):
+        o.poison()
+    route.fused(plan, xd, w, wr, ref.latent, ref.logits, ref.ids, ref.weights, ws, rows=rows)
+    route.fused_packed(plan, xd, packed, got.latent, got.logits, got.ids, got.weights, ws, rows=rows)
+    torch.cuda.synchronize()
+    r, g = ref.host(), got.host()
+    log(f"prefill tile plan rows={rows}")
+    assert np.array_equal(r["latent"], g["latent"])
+    assert np.array_equal(r["logits"].view(np.uint32), g["logits"].view(np.uint32))
+    assert np.array_equal(r["ids"], g["ids"])
+    assert np.array_equal(r["weights"].view(np.uint32), g["weights"].view(np.uint32))
+    check_outputs(xs, g, f"prefill tile plan rows={rows}")
