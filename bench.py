@@ -533,7 +533,11 @@ def main():
         packed = p["packed"]
         t_all = t_call(lambda: route.fused_packed(plan, x, packed, lat, lg, ids, wt, ws), args.prefill_reps)
         t_lr = t_call(lambda: route.latent_router_packed(plan, x, packed, lat, lg, ws), args.prefill_reps)
-        t_tk = t_call(lambda: route.topk16(plan, lg, ids, wt), args.prefill_reps)
+        # one top-16 call is shorter than its host-side launch, so eager calls
+        # would time the host: time a graph of 20 calls instead
+        g_tk = capture_graph(lambda: [route.topk16(plan, lg, ids, wt) for _ in range(20)], torch)
+        t_tk = t_call(lambda: g_tk.replay(), args.prefill_reps) / 20
+        del g_tk
         clocks["prefill_gemms"] = sample_sclk(
             lambda: [route.latent_router_packed(plan, x, packed, lat, lg, ws) for _ in range(10)], torch)
         t_all_kn = t_call(lambda: route.fused(plan, x, w0, wr0, lat, lg, ids, wt, ws), args.prefill_reps)
